@@ -1,0 +1,186 @@
+"""fp64 CPU oracle for static sparse spatiotemporal attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` import this package.  The product
+library (``static_sparse_spatiotemporal_amd``) never imports, links or calls
+it, and it imports nothing from the product.
+
+Definitions followed (pages on the method; see ``oracle.h`` for detail):
+  * Radial Attention, section 2, eq. 1 and eq. 2 -- (masked) softmax attention
+  * Radial Attention, section 3, eq. 4 -- the radial mask over frames/positions
+  * Token Radius Attention, radius design section -- (r_t, r_s) neighbourhood
+  * Vera 1.1 temporal module, sections 2.1-2.2 -- frame sliding-window causal
+  * Radial Attention, section 6 -- 128 x 128 block granularity
+
+The C part (``oracle.c``) does the arithmetic; this module only marshals numpy
+arrays through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+DENSE, RADIAL, RADIUS3D, SWA = 0, 1, 2, 3
+ELEMENT, BLOCK_ANY = 0, 1
+F32, BF16 = 0, 1
+
+KIND_BY_NAME = {"dense": DENSE, "radial": RADIAL, "radius3d": RADIUS3D, "swa": SWA}
+GRAN_BY_NAME = {"element": ELEMENT, "block_any": BLOCK_ANY}
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (plain -O2, pthreads)."""
+    src = os.path.join(_HERE, "oracle.c")
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(src):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, src, "-lm", "-lpthread"],
+                   check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Mask(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("granularity", ctypes.c_int32),
+                ("f", ctypes.c_int64), ("s", ctypes.c_int64), ("block", ctypes.c_int64),
+                ("grid_h", ctypes.c_int64), ("grid_w", ctypes.c_int64),
+                ("r_t", ctypes.c_int64), ("r_s", ctypes.c_int64), ("window", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.POINTER
+        lib.orc_keep.argtypes = [P(_Mask), ctypes.c_int64, ctypes.c_int64]
+        lib.orc_keep.restype = ctypes.c_int
+        lib.orc_elem_matrix.argtypes = [P(_Mask), ctypes.c_void_p]
+        lib.orc_block_counts.argtypes = [P(_Mask), ctypes.c_void_p, ctypes.c_int]
+        lib.orc_kept_elements.argtypes = [P(_Mask), ctypes.c_int]
+        lib.orc_kept_elements.restype = ctypes.c_int64
+        lib.orc_block_bits128.argtypes = [P(_Mask), ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        lib.orc_attention_rows.argtypes = [
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            P(_Mask), ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+class MaskSpec:
+    """A mask family with its parameters (kind and granularity by name)."""
+
+    def __init__(self, kind: str, f: int, s: int, granularity: str = "element", block: int = 128,
+                 grid_h: int = 0, grid_w: int = 0, r_t: int = 0, r_s: int = 0, window: int = 0):
+        self.kind, self.granularity = kind, granularity
+        self.f, self.s, self.block = int(f), int(s), int(block)
+        self.grid_h, self.grid_w = int(grid_h), int(grid_w)
+        self.r_t, self.r_s, self.window = int(r_t), int(r_s), int(window)
+
+    @property
+    def n(self) -> int:
+        return self.f * self.s
+
+    @property
+    def nb(self) -> int:
+        return (self.n + self.block - 1) // self.block
+
+    def _c(self) -> _Mask:
+        return _Mask(KIND_BY_NAME[self.kind], GRAN_BY_NAME[self.granularity], self.f, self.s,
+                     self.block, self.grid_h, self.grid_w, self.r_t, self.r_s, self.window)
+
+
+def keep(spec: MaskSpec, q: int, t: int) -> bool:
+    m = spec._c()
+    return bool(_load().orc_keep(ctypes.byref(m), q, t))
+
+
+def element_matrix(spec: MaskSpec) -> np.ndarray:
+    """n x n uint8 matrix of the element predicate (1 = kept, i.e. M = 0)."""
+    out = np.zeros((spec.n, spec.n), dtype=np.uint8)
+    m = spec._c()
+    _load().orc_elem_matrix(ctypes.byref(m), out.ctypes.data)
+    return out
+
+
+def block_counts(spec: MaskSpec, threads: int | None = None) -> np.ndarray:
+    """nb x nb int64 kept-element counts per block (edge spec.block)."""
+    out = np.zeros((spec.nb, spec.nb), dtype=np.int64)
+    m = spec._c()
+    _load().orc_block_counts(ctypes.byref(m), out.ctypes.data, threads or default_threads())
+    return out
+
+
+def kept_elements(spec: MaskSpec, threads: int | None = None) -> int:
+    m = spec._c()
+    return int(_load().orc_kept_elements(ctypes.byref(m), threads or default_threads()))
+
+
+def block_bits128(spec: MaskSpec, qb: int, kb: int) -> np.ndarray:
+    """128 x 4 uint32 row bitmaps of block (qb, kb); requires spec.block == 128."""
+    assert spec.block == 128
+    out = np.zeros((128, 4), dtype=np.uint32)
+    m = spec._c()
+    _load().orc_block_bits128(ctypes.byref(m), qb, kb, out.ctypes.data)
+    return out
+
+
+def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, spec: MaskSpec,
+                   rows: np.ndarray | None = None, scale: float | None = None,
+                   block_keep: np.ndarray | None = None, threads: int | None = None):
+    """fp64 masked attention (eq. 2) for selected rows.
+
+    q, k, v: [B, H, n, d] numpy arrays, float32 or uint16 (raw bfloat16 bits).
+    rows: int64 array of (b, h, query) triples; None = every row.
+    Returns (O [nrows, d] float64, LSE [nrows] float64).
+    """
+    B, H, n, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape and n == spec.n
+    if q.dtype == np.float32:
+        dtype = F32
+    elif q.dtype == np.uint16:
+        dtype = BF16
+    else:
+        raise TypeError("q/k/v must be float32 or uint16 (bfloat16 bits)")
+    assert k.dtype == q.dtype and v.dtype == q.dtype
+    q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+    if rows is None:
+        bb, hh, qq = np.meshgrid(np.arange(B), np.arange(H), np.arange(n), indexing="ij")
+        rows = np.stack([bb.ravel(), hh.ravel(), qq.ravel()], axis=1)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    bk_ptr = None
+    if spec.granularity == "block_any":
+        if block_keep is None:
+            block_keep = block_counts(spec, threads) > 0
+        block_keep = np.ascontiguousarray(block_keep, dtype=np.uint8)
+        assert block_keep.shape == (spec.nb, spec.nb)
+        bk_ptr = block_keep.ctypes.data
+    o = np.zeros((rows.shape[0], d), dtype=np.float64)
+    lse = np.zeros((rows.shape[0],), dtype=np.float64)
+    m = spec._c()
+    _load().orc_attention_rows(dtype, q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, n, d,
+                               ctypes.byref(m), bk_ptr, float(scale), rows.ctypes.data,
+                               rows.shape[0], o.ctypes.data, lse.ctypes.data,
+                               threads or default_threads())
+    return o, lse

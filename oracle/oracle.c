@@ -1,0 +1,298 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle (see oracle.h for what it computes and
+ * where each definition comes from).
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and the
+ * benchmark's CPU-baseline leg; never by the product library.
+ *
+ * Deliberately slow and literal: every mask entry is evaluated from the
+ * element predicate, and attention visits every key of a row and skips the
+ * masked ones (exp(-inf) = 0 contributes nothing to eq. 2's softmax).
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+static int64_t iabs64(int64_t x) { return x < 0 ? -x : x; }
+
+/* floor(log2(x)) for x >= 1, as bit length minus one. */
+static int64_t floor_log2(int64_t x)
+{
+    int64_t r = -1;
+    while (x > 0) {
+        r++;
+        x >>= 1;
+    }
+    return r;
+}
+
+/* Radial Attention, section 3, eq. 4.  With r = floor(log2(max(|i-j|, 1)))
+ * an entry is kept when
+ *   (a) 2^r <= s and |k - l| + 1 <= s / 2^r, or
+ *   (b) |i - j| mod ceil(2^r / s) == 0 and k == l.
+ * (a) is tested as (|k - l| + 1) * 2^r <= s, the same inequality multiplied
+ * by 2^r > 0, so no real division is needed. */
+static int keep_radial(int64_t s, int64_t q, int64_t t)
+{
+    int64_t i = q / s, k = q % s;
+    int64_t j = t / s, l = t % s;
+    int64_t delta = iabs64(i - j);
+    int64_t r = floor_log2(delta > 1 ? delta : 1);
+    int64_t p2 = (int64_t)1 << r;
+    if (p2 <= s && (iabs64(k - l) + 1) * p2 <= s)
+        return 1;
+    int64_t stride = (p2 + s - 1) / s; /* ceil(2^r / s) */
+    if (delta % stride == 0 && k == l)
+        return 1;
+    return 0;
+}
+
+/* Token radius neighbourhood on a (T, H, W) grid flattened t-h-w:
+ * |dt| <= r_t and max(|dh|, |dw|) <= r_s. */
+static int keep_radius3d(const orc_mask *m, int64_t q, int64_t t)
+{
+    int64_t hw = m->grid_h * m->grid_w;
+    int64_t tq = q / hw, hq = (q % hw) / m->grid_w, wq = q % m->grid_w;
+    int64_t tk = t / hw, hk = (t % hw) / m->grid_w, wk = t % m->grid_w;
+    int64_t dh = iabs64(hq - hk), dw = iabs64(wq - wk);
+    int64_t cheb = dh > dw ? dh : dw;
+    return iabs64(tq - tk) <= m->r_t && cheb <= m->r_s;
+}
+
+/* Vera 1.1 temporal module, section 2.2: query frame i sees key frames
+ * max(0, i - W + 1) .. i (causal AND window), all tokens of those frames. */
+static int keep_swa(const orc_mask *m, int64_t q, int64_t t)
+{
+    int64_t i = q / m->s, j = t / m->s;
+    int64_t lo = i - m->window + 1;
+    if (lo < 0)
+        lo = 0;
+    return j >= lo && j <= i;
+}
+
+int orc_keep(const orc_mask *m, int64_t q, int64_t t)
+{
+    switch (m->kind) {
+    case ORC_DENSE:
+        return 1;
+    case ORC_RADIAL:
+        return keep_radial(m->s, q, t);
+    case ORC_RADIUS3D:
+        return keep_radius3d(m, q, t);
+    case ORC_SWA:
+        return keep_swa(m, q, t);
+    default:
+        return 0;
+    }
+}
+
+void orc_elem_matrix(const orc_mask *m, uint8_t *out)
+{
+    int64_t n = m->f * m->s;
+    for (int64_t q = 0; q < n; q++)
+        for (int64_t t = 0; t < n; t++)
+            out[q * n + t] = (uint8_t)orc_keep(m, q, t);
+}
+
+/* ---- block counts (threaded over block rows) ---------------------------- */
+
+typedef struct {
+    const orc_mask *m;
+    int64_t *out;
+    int64_t row_begin, row_end, nb, n;
+} count_job;
+
+static void *count_worker(void *arg)
+{
+    count_job *j = (count_job *)arg;
+    const int64_t bsz = j->m->block;
+    for (int64_t bq = j->row_begin; bq < j->row_end; bq++) {
+        for (int64_t bk = 0; bk < j->nb; bk++) {
+            int64_t c = 0;
+            for (int64_t q = bq * bsz; q < (bq + 1) * bsz && q < j->n; q++)
+                for (int64_t t = bk * bsz; t < (bk + 1) * bsz && t < j->n; t++)
+                    c += orc_keep(j->m, q, t);
+            j->out[bq * j->nb + bk] = c;
+        }
+    }
+    return NULL;
+}
+
+void orc_block_counts(const orc_mask *m, int64_t *out, int threads)
+{
+    int64_t n = m->f * m->s;
+    int64_t nb = (n + m->block - 1) / m->block;
+    if (threads < 1)
+        threads = 1;
+    if (threads > nb)
+        threads = (int)nb;
+    count_job *jobs = (count_job *)calloc((size_t)threads, sizeof(count_job));
+    pthread_t *tid = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    for (int w = 0; w < threads; w++) {
+        jobs[w].m = m;
+        jobs[w].out = out;
+        jobs[w].nb = nb;
+        jobs[w].n = n;
+        jobs[w].row_begin = nb * w / threads;
+        jobs[w].row_end = nb * (w + 1) / threads;
+        pthread_create(&tid[w], NULL, count_worker, &jobs[w]);
+    }
+    for (int w = 0; w < threads; w++)
+        pthread_join(tid[w], NULL);
+    free(jobs);
+    free(tid);
+}
+
+int64_t orc_kept_elements(const orc_mask *m, int threads)
+{
+    int64_t n = m->f * m->s;
+    int64_t nb = (n + m->block - 1) / m->block;
+    int64_t *cnt = (int64_t *)malloc((size_t)(nb * nb) * sizeof(int64_t));
+    orc_block_counts(m, cnt, threads);
+    int64_t tot = 0;
+    for (int64_t i = 0; i < nb * nb; i++)
+        tot += cnt[i];
+    free(cnt);
+    return tot;
+}
+
+void orc_block_bits128(const orc_mask *m, int64_t qb, int64_t kb, uint32_t *out)
+{
+    int64_t n = m->f * m->s;
+    memset(out, 0, 128 * 4 * sizeof(uint32_t));
+    for (int64_t r = 0; r < 128; r++) {
+        int64_t q = qb * 128 + r;
+        if (q >= n)
+            continue;
+        for (int64_t c = 0; c < 128; c++) {
+            int64_t t = kb * 128 + c;
+            if (t < n && orc_keep(m, q, t))
+                out[r * 4 + c / 32] |= (uint32_t)1 << (c % 32);
+        }
+    }
+}
+
+/* ---- attention ---------------------------------------------------------- */
+
+static double load_value(int dtype, const void *base, int64_t idx)
+{
+    if (dtype == ORC_F32)
+        return (double)((const float *)base)[idx];
+    /* bfloat16 is the upper half of an IEEE binary32: widen by shifting. */
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+typedef struct {
+    int dtype;
+    const void *q, *k, *v;
+    int64_t H, n, d;
+    const orc_mask *mask;
+    const uint8_t *block_keep;
+    double scale;
+    const int64_t *rows;
+    int64_t begin, end;
+    double *o_out, *lse_out;
+} attn_job;
+
+static int key_kept(const attn_job *j, int64_t q, int64_t t)
+{
+    if (j->mask->granularity == ORC_BLOCK_ANY) {
+        int64_t nb = (j->n + j->mask->block - 1) / j->mask->block;
+        return j->block_keep[(q / j->mask->block) * nb + t / j->mask->block] != 0;
+    }
+    return orc_keep(j->mask, q, t);
+}
+
+static void *attn_worker(void *arg)
+{
+    attn_job *j = (attn_job *)arg;
+    const int64_t n = j->n, d = j->d;
+    double *score = (double *)malloc((size_t)n * sizeof(double));
+    double *qrow = (double *)malloc((size_t)d * sizeof(double));
+    for (int64_t r = j->begin; r < j->end; r++) {
+        int64_t b = j->rows[3 * r], h = j->rows[3 * r + 1], q = j->rows[3 * r + 2];
+        int64_t head = (b * j->H + h) * n * d; /* element offset of [b, h, 0, 0] */
+        double *o = j->o_out + r * d;
+        for (int64_t x = 0; x < d; x++) {
+            qrow[x] = load_value(j->dtype, j->q, head + q * d + x);
+            o[x] = 0.0;
+        }
+        /* eq. 2: scaled scores of the kept keys; the max makes exp stable. */
+        double mx = -INFINITY;
+        for (int64_t t = 0; t < n; t++) {
+            if (!key_kept(j, q, t)) {
+                score[t] = -INFINITY;
+                continue;
+            }
+            double acc = 0.0;
+            for (int64_t x = 0; x < d; x++)
+                acc += qrow[x] * load_value(j->dtype, j->k, head + t * d + x);
+            score[t] = acc * j->scale;
+            if (score[t] > mx)
+                mx = score[t];
+        }
+        if (mx == -INFINITY) {
+            j->lse_out[r] = -INFINITY;
+            continue;
+        }
+        double denom = 0.0;
+        for (int64_t t = 0; t < n; t++) {
+            if (score[t] == -INFINITY)
+                continue;
+            double p = exp(score[t] - mx);
+            denom += p;
+            for (int64_t x = 0; x < d; x++)
+                o[x] += p * load_value(j->dtype, j->v, head + t * d + x);
+        }
+        for (int64_t x = 0; x < d; x++)
+            o[x] /= denom;
+        j->lse_out[r] = mx + log(denom);
+    }
+    free(score);
+    free(qrow);
+    return NULL;
+}
+
+void orc_attention_rows(int dtype, const void *q, const void *k, const void *v,
+                        int64_t B, int64_t H, int64_t n, int64_t d,
+                        const orc_mask *mask, const uint8_t *block_keep,
+                        double scale, const int64_t *rows, int64_t nrows,
+                        double *o_out, double *lse_out, int threads)
+{
+    (void)B;
+    if (threads < 1)
+        threads = 1;
+    if (threads > nrows)
+        threads = nrows > 0 ? (int)nrows : 1;
+    attn_job *jobs = (attn_job *)calloc((size_t)threads, sizeof(attn_job));
+    pthread_t *tid = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    for (int w = 0; w < threads; w++) {
+        attn_job *j = &jobs[w];
+        j->dtype = dtype;
+        j->q = q;
+        j->k = k;
+        j->v = v;
+        j->H = H;
+        j->n = n;
+        j->d = d;
+        j->mask = mask;
+        j->block_keep = block_keep;
+        j->scale = scale;
+        j->rows = rows;
+        j->begin = nrows * w / threads;
+        j->end = nrows * (w + 1) / threads;
+        j->o_out = o_out;
+        j->lse_out = lse_out;
+        pthread_create(&tid[w], NULL, attn_worker, j);
+    }
+    for (int w = 0; w < threads; w++)
+        pthread_join(tid[w], NULL);
+    free(jobs);
+    free(tid);
+}

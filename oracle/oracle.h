@@ -1,0 +1,91 @@
+/*
+ * oracle.h -- plain fp64 CPU oracle for static sparse spatiotemporal attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls, links or
+ * includes this file.  Only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark load liboracle.so.  It shares no code, header, table or
+ * constant with the HIP path.
+ *
+ * What it computes (sources are the pages on the method):
+ *   - Radial Attention, section 2 eq. 2: softmax((Q K^T + M) / sqrt(d)) V with
+ *     M in {-inf, 0}^{n x n}; an all-zero M is eq. 1 (standard attention).
+ *   - Radial Attention, section 3 eq. 4: the 4-D radial mask over
+ *     (query frame i, key frame j, query position k, key position l); the
+ *     token index of (frame, position) is frame * s + position (section 1,
+ *     the p_{js+l} index of eq. 3).
+ *   - Token Radius Attention (both blog pages, "radius" design section): a
+ *     token attends to the keys within temporal radius r_t and spatial radius
+ *     r_s on the (t, h, w) token grid flattened t-h-w (3-D patch embedding
+ *     section); keys outside the grid do not exist (no padding).
+ *   - Vera 1.1 temporal module, section 2.1/2.2: frame-level causal sliding
+ *     window, query frame i sees key frames [max(0, i - W + 1), i].
+ *   - Radial Attention, section 6: sparsity is applied on 128 x 128 blocks; a
+ *     block-granularity mask keeps a whole block iff any element is kept.
+ *
+ * All mask arithmetic is integer.  Attention is fp64 over the exact input
+ * values (bf16 or fp32, widened exactly).
+ */
+#ifndef TRA_ORACLE_H
+#define TRA_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_DENSE = 0, ORC_RADIAL = 1, ORC_RADIUS3D = 2, ORC_SWA = 3 };
+enum { ORC_ELEMENT = 0, ORC_BLOCK_ANY = 1 };
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+
+typedef struct {
+    int32_t kind;         /* ORC_* family                                    */
+    int32_t granularity;  /* ORC_ELEMENT or ORC_BLOCK_ANY                    */
+    int64_t f, s;         /* frames, tokens per frame; n = f * s             */
+    int64_t block;        /* block edge for block granularity / counting     */
+    int64_t grid_h, grid_w; /* RADIUS3D: s == grid_h * grid_w                */
+    int64_t r_t, r_s;     /* RADIUS3D radii                                  */
+    int64_t window;       /* SWA: frames seen, the current one included      */
+} orc_mask;
+
+/* Element predicate of the family (granularity ignored): 1 = kept (M = 0). */
+int orc_keep(const orc_mask *m, int64_t q, int64_t t);
+
+/* Dense n x n element matrix of the family's predicate (row = query). */
+void orc_elem_matrix(const orc_mask *m, uint8_t *out);
+
+/* Kept-element count of every (block-row, block-col) block of edge m->block
+ * under the element predicate; blocks at the tail are cut at n.  Out holds
+ * nb x nb int64 with nb = ceil(n / block).  Threads > 1 split block rows. */
+void orc_block_counts(const orc_mask *m, int64_t *out, int threads);
+
+/* Total kept elements of the element predicate. */
+int64_t orc_kept_elements(const orc_mask *m, int threads);
+
+/* Row-major 128-bit-per-row bitmap of one block (block edge m->block, which
+ * must be 128 here): out[r * 4 + w] bit b = element (row qb*128 + r,
+ * key kb*128 + w*32 + b) kept; elements beyond n read as 0. */
+void orc_block_bits128(const orc_mask *m, int64_t qb, int64_t kb, uint32_t *out);
+
+/* fp64 masked attention for a list of rows.
+ *   q, k, v : [B, H, n, d] contiguous, dtype ORC_F32 (float) or ORC_BF16
+ *             (raw bfloat16 bit patterns, uint16)
+ *   mask    : the family; with ORC_BLOCK_ANY a key is kept iff its block
+ *             is kept in block_keep (nb x nb bytes, row = query block), which
+ *             the caller fills from orc_block_counts (> 0).  block_keep is
+ *             ignored for ORC_ELEMENT.
+ *   scale   : multiplies Q K^T (1/sqrt(d) for eq. 1 and eq. 2)
+ *   rows    : nrows triples (b, h, query index)
+ *   o_out   : nrows x d; lse_out: nrows (natural log of the softmax
+ *             denominator of the scaled scores).  A row with no kept key
+ *             gets O = 0 and LSE = -inf.
+ */
+void orc_attention_rows(int dtype, const void *q, const void *k, const void *v,
+                        int64_t B, int64_t H, int64_t n, int64_t d,
+                        const orc_mask *mask, const uint8_t *block_keep,
+                        double scale, const int64_t *rows, int64_t nrows,
+                        double *o_out, double *lse_out, int threads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
