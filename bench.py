@@ -1,0 +1,263 @@
+"""Throughput of the block-sparse attention forward on one MI355X.
+
+One step = one tra_sparse_attn_fwd call (Q K^T, element masks, online softmax,
+P V, epilogue) over the whole workload, with Q/K/V resident in HBM and the
+static mask compiled beforehand (its build time is reported separately).
+
+Prints one JSON line.  `value` is effective TFLOP/s on kept 128 x 128 blocks
+(4 * D * 128^2 flop per kept block per (batch, head)), `ms_per_step` the
+wall-clock ms per call.  The roofline object prices the attention kernel's
+own launches (HIP events on the stream it runs on) against the bf16 dense
+MFMA peak; `cpu_baseline` times the fp64 oracle on a bounded sample of the
+same workload on the host cores.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for fn in ("attn_fwd_bf16.hip", "attn_common.h", "tra_internal.h"):
+        with open(os.path.join(ROOT, "static_sparse_spatiotemporal_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the attention kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(PROFILES, f"attn_fwd_bf16_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        m = re.match(r"^\s*([a-z_]+)\s*:\s*(\S+)", line)
+        if m:
+            fields[m.group(1)] = m.group(2)
+    if fields.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, mask_info, target_s: float):
+    """fp64 oracle on sampled rows of the workload; returns the JSON object."""
+    import oracle
+    import workloads
+    from oracle import MaskSpec
+
+    spec = MaskSpec(w.kind, w.f, w.s, granularity=w.granularity, grid_h=w.grid_h, grid_w=w.grid_w,
+                    r_t=w.r_t, r_s=w.r_s, window=w.window)
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(w.seed)
+    nb = spec.nb
+    heads = [(0, 0), (0, w.H - 1)] if w.H > 1 else [(0, 0)]
+    qblocks = sorted(set(rng.choice(nb, size=min(nb, 32), replace=False).tolist()))
+    block_keep = None
+    if spec.granularity == "block_any":
+        counts = oracle.block_counts_rows(spec, qblocks, threads)
+        block_keep = np.zeros((nb, nb), dtype=np.uint8)
+        block_keep[qblocks] = counts > 0
+    sel = lambda x: np.stack([workloads.to_oracle_array(x[b, h]) for b, h in heads])[None]
+    qa, ka, va = sel(q), sel(k), sel(v)
+    cand = np.array([(0, hi, qb * 128 + r) for hi in range(len(heads)) for qb in qblocks
+                     for r in range(128) if qb * 128 + r < spec.n], dtype=np.int64)
+    cand = cand[rng.permutation(len(cand))]
+
+    def kept_keys(rows):
+        if block_keep is not None:
+            cols = np.minimum(128, spec.n - np.arange(nb) * 128)
+            return np.array([(block_keep[r // 128] > 0) @ cols for r in rows[:, 2]], dtype=np.int64)
+        return np.array([sum(oracle.keep(spec, int(r), t) for t in range(spec.n)) for r in rows[:, 2]])
+
+    # calibrate on a few rows, then size the sample to about target_s seconds
+    probe = cand[:threads]
+    t0 = time.perf_counter()
+    oracle.attention_rows(qa, ka, va, spec, rows=probe, block_keep=block_keep, threads=threads)
+    dt = max(time.perf_counter() - t0, 1e-3)
+    nrows = int(min(len(cand), max(threads, threads * int(target_s / dt))))
+    rows = cand[:nrows]
+    t0 = time.perf_counter()
+    oracle.attention_rows(qa, ka, va, spec, rows=rows, block_keep=block_keep, threads=threads)
+    elapsed = time.perf_counter() - t0
+    flops = float(4 * w.D * kept_keys(rows).sum())
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{nrows} query rows (fp64, all their kept keys) drawn from {len(qblocks)} query blocks "
+                   f"of heads {[h for _, h in heads]}, {elapsed:.1f} s on {threads} threads"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 2 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import static_sparse_spatiotemporal_amd as tra
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        x = torch.empty(1 << 30, dtype=torch.int16, device=dev).fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": x.numel() * 2, "bytes_written": y.numel() * 2}))
+        return
+
+    name = args.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[name]
+    stream = torch.cuda.current_stream()
+
+    t0 = time.perf_counter()
+    mask = tra.build_mask(w.f, w.s, w.kind, **w.mask_kwargs())
+    torch.cuda.synchronize()
+    build_ms = (time.perf_counter() - t0) * 1e3
+    info = mask.info
+    q, k, v = workloads.make_qkv(w, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    for _ in range(args.warmup):
+        tra.sparse_attn_fwd(q, k, v, mask, out=out, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        tra.sparse_attn_fwd(q, k, v, mask, out=out, lse=lse, stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ms_per_step = wall * 1e3 / args.steps
+    launch_ms = float(ev_ms.mean())
+
+    bh = w.B * w.H
+    flops_blocks = 4.0 * w.D * 128 * 128 * info["kept_blocks"] * bh
+    flops_elems = 4.0 * w.D * info["kept_elems"] * bh
+    flops_pred = 4.0 * w.D * info["pred_elems"] * bh
+    value = flops_blocks / (ms_per_step * 1e-3) / 1e12
+    achieved = flops_blocks / (launch_ms * 1e-3) / 1e12
+    traffic = measured_traffic(name)
+    alg_bytes = (4 * bh * w.n * w.D * (2 if w.dtype == "bf16" else 4) + 4 * bh * w.n
+                 + 8 * info["kept_blocks"] + 2048 * info["partial_blocks"])
+
+    extra = {
+        "mask_build_ms": round(build_ms, 3),
+        "launch_ms_mean": round(launch_ms, 4),
+        "launch_ms_p10": round(float(np.percentile(ev_ms, 10)), 4),
+        "launch_ms_p90": round(float(np.percentile(ev_ms, 90)), 4),
+        "tflops_kept_elements": round(flops_elems / (launch_ms * 1e-3) / 1e12, 2),
+        "tflops_eq4_elements": round(flops_pred / (launch_ms * 1e-3) / 1e12, 2),
+        "pct_bf16_peak": round(100 * achieved / BF16_PEAK_TFLOPS, 2),
+        "algorithmic_bytes": alg_bytes,
+        "algorithmic_gbs": round(alg_bytes / (launch_ms * 1e-3) / 1e9, 1),
+    }
+    mask.free()
+
+    if not args.no_dense and w.kind != "dense" and name == workloads.HEADLINE:
+        dmask = tra.build_mask(w.f, w.s, "dense", granularity="block_any")
+        tra.sparse_attn_fwd(q, k, v, dmask, out=out, lse=lse, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        e0.record(stream)
+        for _ in range(reps):
+            tra.sparse_attn_fwd(q, k, v, dmask, out=out, lse=lse, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / reps
+        dflops = 4.0 * w.D * 128 * 128 * dmask.info["kept_blocks"] * bh
+        extra.update({"dense_ms": round(dense_ms, 3),
+                      "dense_tflops": round(dflops / (dense_ms * 1e-3) / 1e12, 2),
+                      "speedup_vs_dense": round(dense_ms / launch_ms, 3)})
+        dmask.free()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, q, k, v, info, args.cpu_seconds)
+
+    line = {
+        "metric": "ms/call + effective TFLOP/s on kept blocks (% of bf16 MFMA peak) at n=131072",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": name,
+            "mask": f"{w.kind} ({w.granularity}), 128x128 blocks",
+            "frames": w.f, "tokens_per_frame": w.s, "n": w.n, "batch": w.B, "heads": w.H,
+            "head_dim": w.D,
+            "kept_blocks_per_head": info["kept_blocks"], "total_blocks_per_head": info["nqb"] * info["nkb"],
+            "block_sparsity": round(1 - info["kept_blocks"] / (info["nqb"] * info["nkb"]), 4),
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * tra.h -- C ABI of the static sparse spatiotemporal attention library
+ * (libtra.so), built for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes masked attention over video tokens,
+ *
+ *     O = softmax((Q K^T + M) * scale) V,   M in {-inf, 0}^{n x n},
+ *
+ * Radial Attention (NeurIPS 2025) section 2, eq. 2 (eq. 1 when M = 0), with
+ * the scale 1/sqrt(d) of those equations unless the caller passes another.
+ * M is static: it depends only on the frame count f, the tokens per frame s
+ * and the family parameters, never on Q, K, V.  The families:
+ *
+ *   TRA_MASK_RADIAL      Radial Attention section 3, eq. 4.  Token index =
+ *                        frame * s + position.  Query (frame i, position k)
+ *                        keeps key (frame j, position l) iff, with
+ *                        r = floor(log2(max(|i-j|, 1))):
+ *                          2^r <= s and |k-l| + 1 <= s / 2^r, or
+ *                          |i-j| mod ceil(2^r / s) == 0 and k == l.
+ *   TRA_MASK_RADIUS3D    Token Radius Attention (radius design section of
+ *                        both blog pages): tokens on a (f, grid_h, grid_w)
+ *                        grid flattened t-h-w; keep iff |dt| <= r_t and
+ *                        max(|dh|, |dw|) <= r_s.  Keys off the grid do not
+ *                        exist (no padding).
+ *   TRA_MASK_SWA_CAUSAL  Vera 1.1 temporal module, sections 2.1-2.2:
+ *                        query frame i keeps every token of key frames
+ *                        max(0, i - window + 1) .. i.
+ *   TRA_MASK_DENSE       every entry kept (eq. 1).
+ *
+ * Radial Attention section 6 applies sparsity on 128 x 128 blocks; the mask
+ * is compiled once into a block bitmap, a per-query-block CSR list of kept
+ * key blocks and 128 x 128 element bitmasks for the kept blocks that are only
+ * partly kept.  TRA_GRAN_BLOCK_ANY keeps a whole block iff any element in it
+ * is kept.
+ *
+ * Conventions for every call:
+ *   - Return TRA_OK (0) or a negative tra_status.  Argument, shape, dtype and
+ *     stride errors are detected on the host before anything is enqueued.
+ *   - Device work is asynchronous on the caller's HIP stream (NULL = the
+ *     default stream); faults inside kernels surface at the caller's next
+ *     synchronisation.  TRA_ERR_HIP means a HIP runtime call failed; its
+ *     hipError_t is kept in tra_last_hip_error() (per thread).
+ *   - Device pointers are HIP device (or managed) memory of the current
+ *     device.  No call keeps a pointer to caller memory after it returns.
+ */
+#ifndef TRA_H
+#define TRA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TRA_OK = 0,
+    TRA_ERR_INVALID = -1,     /* null pointer, value out of range           */
+    TRA_ERR_UNSUPPORTED = -2, /* valid request this build does not handle   */
+    TRA_ERR_SHAPE = -3,       /* tensor shapes disagree with each other/mask */
+    TRA_ERR_OOM = -4,         /* device allocation failed                   */
+    TRA_ERR_HIP = -5          /* other HIP runtime failure                  */
+} tra_status;
+
+typedef enum {
+    TRA_MASK_DENSE = 0,
+    TRA_MASK_RADIAL = 1,
+    TRA_MASK_RADIUS3D = 2,
+    TRA_MASK_SWA_CAUSAL = 3
+} tra_mask_kind;
+
+typedef enum {
+    TRA_GRAN_ELEMENT = 0,   /* exact element mask; partial blocks carry bits */
+    TRA_GRAN_BLOCK_ANY = 1  /* 128 x 128 block kept iff any element kept     */
+} tra_granularity;
+
+typedef enum { TRA_F32 = 0, TRA_BF16 = 1 } tra_dtype;
+
+/* Family parameters.  Fields a family does not use must be 0.
+ *   granularity  tra_granularity
+ *   block        block edge; must be 0 (= 128) or 128
+ *   grid_h/w     RADIUS3D: s == grid_h * grid_w, grid_h, grid_w >= 1
+ *   r_t, r_s     RADIUS3D radii, >= 0
+ *   window       SWA_CAUSAL: frames seen including the current one, >= 1
+ *   reserved     must be 0                                                  */
+typedef struct {
+    int32_t granularity;
+    int32_t block;
+    int32_t grid_h, grid_w;
+    int32_t r_t, r_s;
+    int32_t window;
+    int32_t reserved[9];
+} tra_mask_params;
+
+typedef struct tra_mask tra_mask; /* opaque; owns its device buffers */
+
+typedef struct {
+    int64_t n;              /* tokens = f * s                               */
+    int64_t f, s;
+    int64_t nqb, nkb;       /* query / key blocks = ceil(n / 128)           */
+    int64_t kept_blocks;    /* CSR entries (non-empty blocks)               */
+    int64_t partial_blocks; /* kept blocks that carry an element bitmask    */
+    int64_t kept_elems;     /* (q, t) pairs, q, t < n, attended per (b, h)  */
+    int64_t pred_elems;     /* pairs kept by the family's element predicate */
+    int64_t min_row_blocks, max_row_blocks;
+    int64_t bitmap_words;   /* uint32 words per bitmap row = ceil(nkb / 32) */
+    int32_t kind, granularity;
+} tra_mask_info;
+
+/* A [B, H, N, D] tensor view.  stride[] in elements, order B, H, N, D;
+ * stride[3] must be 1; stride[2] (row pitch) a multiple of 8 elements and
+ * data 16-byte aligned. */
+typedef struct {
+    void *data;
+    int32_t dtype; /* tra_dtype */
+    int32_t reserved;
+    int64_t B, H, N, D;
+    int64_t stride[4];
+} tra_tensor;
+
+/*
+ * tra_build_mask -- compile the static mask for n = f * s tokens.
+ *
+ * Defines M of eq. 2 from the family (see the list at the top of this file)
+ * and stores it at 128 x 128 block granularity (Radial Attention section 6).
+ * f >= 1, s >= 1, n < 2^31.  n need not be a multiple of 128: the last
+ * block row/column is cut at n and every kept block that reaches past n
+ * carries an element bitmask that drops the missing keys.
+ *
+ * Runs the mask-builder kernels on `hip_stream` and waits for them (the build
+ * is synchronous; it is meant to run once per (f, s, kind, params)).  On
+ * success *out owns device memory until tra_mask_free.  On failure *out is
+ * NULL.  Errors: TRA_ERR_INVALID (null out/params, f or s < 1, unknown kind
+ * or granularity, negative radius, window < 1, nonzero unused field),
+ * TRA_ERR_UNSUPPORTED (block not 0/128, n >= 2^31), TRA_ERR_SHAPE (RADIUS3D
+ * with s != grid_h * grid_w), TRA_ERR_OOM, TRA_ERR_HIP.
+ */
+tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_params *params,
+                          void *hip_stream, tra_mask **out);
+
+/*
+ * tra_sparse_attn_fwd -- O = softmax((Q K^T + M) * scale) V  (eq. 2).
+ *
+ * Q, K, V, O: [B, H, N, D] views, one dtype for all four (TRA_BF16: bf16
+ * inputs, fp32 accumulation, O rounded to nearest-even bf16; TRA_F32: fp32
+ * throughout).  N == mask n; D in {64, 128}.  O must not overlap Q, K or V.
+ * LSE: NULL or device float[B * H * N] (contiguous [B, H, N]) receiving the
+ * natural log of each row's softmax denominator, ln sum_t exp(scale * q.k_t)
+ * over kept keys.  scale <= 0 selects 1/sqrt(D).  Rows whose every key is
+ * masked (impossible for the families above) get O = 0 and LSE = -inf.
+ *
+ * The mask is shared by every (b, h).  Asynchronous on hip_stream; allocates
+ * nothing.  The mask holds the work-queue counter of the kernel, so calls
+ * that use the same mask must not run concurrently (same stream is fine).
+ * B == 0 or H == 0 returns TRA_OK without launching.
+ * Errors: TRA_ERR_INVALID (null tensor/mask/data), TRA_ERR_SHAPE (shapes
+ * disagree or N != n), TRA_ERR_UNSUPPORTED (D not 64/128, mixed dtypes,
+ * bad stride or alignment, more than 2^31 work items), TRA_ERR_HIP.
+ */
+tra_status tra_sparse_attn_fwd(const tra_tensor *Q, const tra_tensor *K, const tra_tensor *V,
+                               const tra_mask *mask, tra_tensor *O, float *LSE, float scale,
+                               void *hip_stream);
+
+/* Copy the host-side summary filled at build time.  No device work. */
+tra_status tra_mask_get_info(const tra_mask *mask, tra_mask_info *out);
+
+/*
+ * tra_mask_export -- copy the compiled mask to host buffers (synchronous).
+ * Any pointer may be NULL to skip that part.  Sizes from tra_mask_info:
+ *   bitmap    uint32[nqb * bitmap_words]; bit (kb % 32) of word
+ *             [qb * bitmap_words + kb / 32] = block (qb, kb) kept
+ *   row_ptr   int32[nqb + 1]; CSR offsets of each query block's kept blocks
+ *   col_idx   int32[kept_blocks]; kept key blocks, ascending within a row
+ *   emask_idx int32[kept_blocks]; -1 = whole block kept, else the index of
+ *             its bitmask (partial blocks numbered in CSR order)
+ *   emask     uint32[partial_blocks * 128 * 4]; row r of a partial block is
+ *             4 words, bit b of word w = key (w * 32 + b) of the block kept
+ *   order     int32[nqb]; query blocks by decreasing kept-block count
+ *             (ties by index), the order the attention kernel takes them
+ */
+tra_status tra_mask_export(const tra_mask *mask, uint32_t *bitmap, int32_t *row_ptr,
+                           int32_t *col_idx, int32_t *emask_idx, uint32_t *emask, int32_t *order);
+
+/* Release the mask's device memory.  NULL is ignored.  The caller makes sure
+ * no kernel that uses the mask is still queued. */
+void tra_mask_free(tra_mask *mask);
+
+/* Static, never-NULL name of a status code. */
+const char *tra_status_string(tra_status s);
+
+/* hipError_t of the last TRA_ERR_HIP / TRA_ERR_OOM returned on this thread
+ * (0 if none). */
+int32_t tra_last_hip_error(void);
+
+/* Library version as 10000 * major + 100 * minor + patch. */
+int32_t tra_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TRA_H */

@@ -67,6 +67,8 @@ def _load():
         lib.orc_keep.restype = ctypes.c_int
         lib.orc_elem_matrix.argtypes = [P(_Mask), ctypes.c_void_p]
         lib.orc_block_counts.argtypes = [P(_Mask), ctypes.c_void_p, ctypes.c_int]
+        lib.orc_block_counts_rows.argtypes = [P(_Mask), ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                              ctypes.c_int]
         lib.orc_kept_elements.argtypes = [P(_Mask), ctypes.c_int]
         lib.orc_kept_elements.restype = ctypes.c_int64
         lib.orc_block_bits128.argtypes = [P(_Mask), ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
@@ -127,6 +129,16 @@ def block_counts(spec: MaskSpec, threads: int | None = None) -> np.ndarray:
     out = np.zeros((spec.nb, spec.nb), dtype=np.int64)
     m = spec._c()
     _load().orc_block_counts(ctypes.byref(m), out.ctypes.data, threads or default_threads())
+    return out
+
+
+def block_counts_rows(spec: MaskSpec, rows, threads: int | None = None) -> np.ndarray:
+    """len(rows) x nb int64 kept-element counts of the listed block rows."""
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, spec.nb), dtype=np.int64)
+    m = spec._c()
+    _load().orc_block_counts_rows(ctypes.byref(m), rows.ctypes.data, rows.size, out.ctypes.data,
+                                  threads or default_threads())
     return out
 
 

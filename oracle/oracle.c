@@ -146,6 +146,57 @@ void orc_block_counts(const orc_mask *m, int64_t *out, int threads)
     free(tid);
 }
 
+typedef struct {
+    const orc_mask *m;
+    const int64_t *rows;
+    int64_t *out;
+    int64_t begin, end, nb, n;
+} count_rows_job;
+
+static void *count_rows_worker(void *arg)
+{
+    count_rows_job *j = (count_rows_job *)arg;
+    const int64_t bsz = j->m->block;
+    for (int64_t i = j->begin; i < j->end; i++) {
+        int64_t bq = j->rows[i];
+        for (int64_t bk = 0; bk < j->nb; bk++) {
+            int64_t c = 0;
+            for (int64_t q = bq * bsz; q < (bq + 1) * bsz && q < j->n; q++)
+                for (int64_t t = bk * bsz; t < (bk + 1) * bsz && t < j->n; t++)
+                    c += orc_keep(j->m, q, t);
+            j->out[i * j->nb + bk] = c;
+        }
+    }
+    return NULL;
+}
+
+void orc_block_counts_rows(const orc_mask *m, const int64_t *rows, int64_t nrows, int64_t *out,
+                           int threads)
+{
+    int64_t n = m->f * m->s;
+    int64_t nb = (n + m->block - 1) / m->block;
+    if (threads < 1)
+        threads = 1;
+    if (threads > nrows)
+        threads = nrows > 0 ? (int)nrows : 1;
+    count_rows_job *jobs = (count_rows_job *)calloc((size_t)threads, sizeof(count_rows_job));
+    pthread_t *tid = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    for (int w = 0; w < threads; w++) {
+        jobs[w].m = m;
+        jobs[w].rows = rows;
+        jobs[w].out = out;
+        jobs[w].nb = nb;
+        jobs[w].n = n;
+        jobs[w].begin = nrows * w / threads;
+        jobs[w].end = nrows * (w + 1) / threads;
+        pthread_create(&tid[w], NULL, count_rows_worker, &jobs[w]);
+    }
+    for (int w = 0; w < threads; w++)
+        pthread_join(tid[w], NULL);
+    free(jobs);
+    free(tid);
+}
+
 int64_t orc_kept_elements(const orc_mask *m, int threads)
 {
     int64_t n = m->f * m->s;

@@ -58,6 +58,11 @@ void orc_elem_matrix(const orc_mask *m, uint8_t *out);
  * nb x nb int64 with nb = ceil(n / block).  Threads > 1 split block rows. */
 void orc_block_counts(const orc_mask *m, int64_t *out, int threads);
 
+/* Same as orc_block_counts for the listed block rows only: out holds
+ * nrows x nb int64, row i = block row rows[i]. */
+void orc_block_counts_rows(const orc_mask *m, const int64_t *rows, int64_t nrows, int64_t *out,
+                           int threads);
+
 /* Total kept elements of the element predicate. */
 int64_t orc_kept_elements(const orc_mask *m, int threads);
 

@@ -1,0 +1,219 @@
+"""Static sparse spatiotemporal attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``libtra.so`` (C ABI in ``include/tra.h``).  This
+module only marshals arguments: torch supplies device memory and the HIP
+stream, and every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is not built, importing the binding's
+functions raises.
+
+    mask = build_mask(f=128, s=1024, kind="radial", granularity="block_any")
+    out, lse = sparse_attn_fwd(q, k, v, mask)      # q, k, v: [B, H, n, D] on cuda
+
+Computes softmax((Q K^T + M) / sqrt(D)) V (Radial Attention section 2, eq. 2)
+with M one of: the radial mask of eq. 4, a (r_t, r_s) token-radius
+neighbourhood on a t-h-w grid, or a frame sliding-window causal mask.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+__all__ = ["build_mask", "sparse_attn_fwd", "Mask", "TraError", "library_path", "load_library",
+           "KINDS", "GRANULARITIES"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libtra.so")
+
+KINDS = {"dense": 0, "radial": 1, "radius3d": 2, "swa": 3}
+GRANULARITIES = {"element": 0, "block_any": 1}
+_F32, _BF16 = 0, 1
+_STATUS = {0: "TRA_OK", -1: "TRA_ERR_INVALID", -2: "TRA_ERR_UNSUPPORTED", -3: "TRA_ERR_SHAPE",
+           -4: "TRA_ERR_OOM", -5: "TRA_ERR_HIP"}
+
+
+class TraError(RuntimeError):
+    def __init__(self, status: int, what: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        extra = f" (hipError {hip_error})" if status in (-4, -5) else ""
+        super().__init__(f"{what}: {_STATUS.get(status, status)}{extra}")
+
+
+class MaskParams(ctypes.Structure):
+    _fields_ = [("granularity", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("r_t", ctypes.c_int32), ("r_s", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 9)]
+
+
+class MaskInfo(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("f", ctypes.c_int64), ("s", ctypes.c_int64),
+                ("nqb", ctypes.c_int64), ("nkb", ctypes.c_int64),
+                ("kept_blocks", ctypes.c_int64), ("partial_blocks", ctypes.c_int64),
+                ("kept_elems", ctypes.c_int64), ("pred_elems", ctypes.c_int64),
+                ("min_row_blocks", ctypes.c_int64), ("max_row_blocks", ctypes.c_int64),
+                ("bitmap_words", ctypes.c_int64), ("kind", ctypes.c_int32),
+                ("granularity", ctypes.c_int32)]
+
+
+class TensorDesc(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("D", ctypes.c_int64), ("stride", ctypes.c_int64 * 4)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libtra.so once.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing; build it with "
+                           "`python -m static_sparse_spatiotemporal_amd._build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    lib.tra_build_mask.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, P(MaskParams), vp, P(vp)]
+    lib.tra_build_mask.restype = ctypes.c_int
+    lib.tra_sparse_attn_fwd.argtypes = [P(TensorDesc), P(TensorDesc), P(TensorDesc), vp, P(TensorDesc),
+                                        vp, ctypes.c_float, vp]
+    lib.tra_sparse_attn_fwd.restype = ctypes.c_int
+    lib.tra_mask_get_info.argtypes = [vp, P(MaskInfo)]
+    lib.tra_mask_get_info.restype = ctypes.c_int
+    lib.tra_mask_export.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    lib.tra_mask_export.restype = ctypes.c_int
+    lib.tra_mask_free.argtypes = [vp]
+    lib.tra_mask_free.restype = None
+    lib.tra_status_string.argtypes = [ctypes.c_int]
+    lib.tra_status_string.restype = ctypes.c_char_p
+    lib.tra_last_hip_error.argtypes = []
+    lib.tra_last_hip_error.restype = ctypes.c_int32
+    lib.tra_version.argtypes = []
+    lib.tra_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise TraError(status, what, load_library().tra_last_hip_error())
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+class Mask:
+    """A compiled static mask (owns device memory until freed)."""
+
+    def __init__(self, handle: ctypes.c_void_p):
+        self._h = handle
+        info = MaskInfo()
+        _check(load_library().tra_mask_get_info(self._h, ctypes.byref(info)), "tra_mask_get_info")
+        self.info = {k: getattr(info, k) for k, _ in MaskInfo._fields_}
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._h is None:
+            raise ValueError("mask was freed")
+        return self._h
+
+    def export(self) -> dict:
+        """Host copies of the compiled mask (see tra_mask_export)."""
+        i = self.info
+        out = {
+            "bitmap": np.zeros((i["nqb"], i["bitmap_words"]), dtype=np.uint32),
+            "row_ptr": np.zeros(i["nqb"] + 1, dtype=np.int32),
+            "col_idx": np.zeros(i["kept_blocks"], dtype=np.int32),
+            "emask_idx": np.zeros(i["kept_blocks"], dtype=np.int32),
+            "emask": np.zeros((i["partial_blocks"], 128, 4), dtype=np.uint32),
+            "order": np.zeros(i["nqb"], dtype=np.int32),
+        }
+        _check(load_library().tra_mask_export(
+            self.handle, *(a.ctypes.data if a.size else None for a in
+                           (out["bitmap"], out["row_ptr"], out["col_idx"], out["emask_idx"],
+                            out["emask"], out["order"]))), "tra_mask_export")
+        return out
+
+    def free(self):
+        if self._h is not None:
+            load_library().tra_mask_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def build_mask(f: int, s: int, kind: str, granularity: str = "element", grid_h: int = 0,
+               grid_w: int = 0, r_t: int = 0, r_s: int = 0, window: int = 0, stream=None) -> Mask:
+    """Compile a static mask for n = f * s tokens (synchronous; see tra_build_mask)."""
+    lib = load_library()
+    p = MaskParams()
+    p.granularity = GRANULARITIES[granularity]
+    p.block = 128
+    p.grid_h, p.grid_w, p.r_t, p.r_s, p.window = grid_h, grid_w, r_t, r_s, window
+    h = ctypes.c_void_p()
+    _check(lib.tra_build_mask(int(f), int(s), KINDS[kind], ctypes.byref(p), _stream_handle(stream),
+                              ctypes.byref(h)), "tra_build_mask")
+    return Mask(h)
+
+
+def _desc(t: torch.Tensor) -> TensorDesc:
+    if t.dim() != 4:
+        raise ValueError("expected a [B, H, N, D] tensor")
+    if t.dtype == torch.bfloat16:
+        dt = _BF16
+    elif t.dtype == torch.float32:
+        dt = _F32
+    else:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    d = TensorDesc()
+    d.data = t.data_ptr()
+    d.dtype = dt
+    d.B, d.H, d.N, d.D = t.shape
+    for i, st in enumerate(t.stride()):
+        d.stride[i] = st
+    return d
+
+
+def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
+                    out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True,
+                    scale: float | None = None, stream=None):
+    """O = softmax((Q K^T + M) * scale) V on the GPU (see tra_sparse_attn_fwd).
+
+    q, k, v: [B, H, n, D] cuda tensors (bf16 or fp32).  `out` defaults to a new
+    contiguous tensor; `lse` = True allocates a [B, H, n] fp32 tensor, a tensor
+    is written in place, False/None skips it.  Returns (out, lse or None).
+    """
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be on a HIP device")
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is True:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != tuple(q.shape[:3])):
+        raise ValueError("lse must be a contiguous float32 [B, H, n] tensor")
+    dq, dk, dv, do = _desc(q), _desc(k), _desc(v), _desc(out)
+    _check(load_library().tra_sparse_attn_fwd(
+        ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), mask.handle, ctypes.byref(do),
+        ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
+        float(scale) if scale else 0.0, _stream_handle(stream)), "tra_sparse_attn_fwd")
+    return out, lse

@@ -1,0 +1,358 @@
+// C ABI of libtra.so: argument checking, mask compilation driver, attention
+// dispatch.  See include/tra.h for the contract of every entry point.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <vector>
+
+#include "tra_internal.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+tra_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return TRA_OK;
+    g_last_hip_error = (int32_t)e;
+    return e == hipErrorOutOfMemory ? TRA_ERR_OOM : TRA_ERR_HIP;
+}
+
+#define TRA_HIP(expr)                              \
+    do {                                           \
+        const hipError_t e_ = (expr);              \
+        if (e_ != hipSuccess) {                    \
+            st_ = hip_status(e_);                  \
+            goto fail;                             \
+        }                                          \
+    } while (0)
+
+template <class T>
+hipError_t dev_alloc(T **p, size_t count)
+{
+    *p = nullptr;
+    return hipMalloc((void **)p, std::max<size_t>(count, 1) * sizeof(T));
+}
+
+void free_mask_buffers(tra_mask *m)
+{
+    hipFree(m->bitmap);
+    hipFree(m->row_ptr);
+    hipFree(m->col_idx);
+    hipFree(m->emask_idx);
+    hipFree(m->emask);
+    hipFree(m->order);
+    hipFree(m->queue);
+}
+
+bool tensor_ok(const tra_tensor *t) { return t != nullptr && t->data != nullptr; }
+
+}  // namespace
+
+extern "C" {
+
+const char *tra_status_string(tra_status s)
+{
+    switch (s) {
+    case TRA_OK:
+        return "TRA_OK";
+    case TRA_ERR_INVALID:
+        return "TRA_ERR_INVALID";
+    case TRA_ERR_UNSUPPORTED:
+        return "TRA_ERR_UNSUPPORTED";
+    case TRA_ERR_SHAPE:
+        return "TRA_ERR_SHAPE";
+    case TRA_ERR_OOM:
+        return "TRA_ERR_OOM";
+    case TRA_ERR_HIP:
+        return "TRA_ERR_HIP";
+    }
+    return "TRA_ERR_UNKNOWN";
+}
+
+int32_t tra_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t tra_version(void) { return 100; /* 0.1.0 */ }
+
+tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_params *p,
+                          void *hip_stream, tra_mask **out)
+{
+    if (out == nullptr || p == nullptr)
+        return TRA_ERR_INVALID;
+    *out = nullptr;
+    if (f < 1 || s < 1)
+        return TRA_ERR_INVALID;
+    if (kind < TRA_MASK_DENSE || kind > TRA_MASK_SWA_CAUSAL)
+        return TRA_ERR_INVALID;
+    if (p->granularity != TRA_GRAN_ELEMENT && p->granularity != TRA_GRAN_BLOCK_ANY)
+        return TRA_ERR_INVALID;
+    for (int i = 0; i < 9; ++i)
+        if (p->reserved[i] != 0)
+            return TRA_ERR_INVALID;
+    if (p->block != 0 && p->block != tra::kBlock)
+        return TRA_ERR_UNSUPPORTED;
+    const bool radius = kind == TRA_MASK_RADIUS3D, swa = kind == TRA_MASK_SWA_CAUSAL;
+    if (!radius && (p->grid_h || p->grid_w || p->r_t || p->r_s))
+        return TRA_ERR_INVALID;
+    if (!swa && p->window)
+        return TRA_ERR_INVALID;
+    if (radius) {
+        if (p->grid_h < 1 || p->grid_w < 1 || p->r_t < 0 || p->r_s < 0)
+            return TRA_ERR_INVALID;
+        if ((int64_t)p->grid_h * p->grid_w != s)
+            return TRA_ERR_SHAPE;
+    }
+    if (swa && p->window < 1)
+        return TRA_ERR_INVALID;
+    if (f > INT32_MAX || s > INT32_MAX || f * s >= ((int64_t)1 << 31))
+        return TRA_ERR_UNSUPPORTED;
+    const int64_t n = f * s;
+    const int64_t nb64 = (n + tra::kBlock - 1) / tra::kBlock;
+    if (nb64 * nb64 >= ((int64_t)1 << 31))
+        return TRA_ERR_UNSUPPORTED;  // block-class matrix indexed with 32 bits
+    const int nqb = (int)nb64, nkb = (int)nb64;
+    const int words = (nkb + 31) / 32;
+
+    tra_mask *m = new (std::nothrow) tra_mask;
+    if (m == nullptr)
+        return TRA_ERR_OOM;
+    std::memset(m, 0, sizeof(*m));
+    tra::MaskDesc &d = m->desc;
+    d.kind = kind;
+    d.granularity = p->granularity;
+    d.n = (int32_t)n;
+    d.f = (int32_t)f;
+    d.s = (int32_t)s;
+    d.grid_h = p->grid_h;
+    d.grid_w = p->grid_w;
+    d.r_t = p->r_t;
+    d.r_s = p->r_s;
+    d.window = p->window;
+
+    hipStream_t st = (hipStream_t)hip_stream;
+    tra_status st_ = TRA_OK;
+    uint8_t *cls = nullptr;
+    int32_t *cnt = nullptr, *row_blocks = nullptr, *row_partial = nullptr, *part_ptr_d = nullptr,
+            *part_list = nullptr;
+    long long *row_pred = nullptr, *row_eff = nullptr;
+    std::vector<int32_t> h_blocks(nqb), h_partial(nqb), h_row_ptr(nqb + 1), h_part_ptr(nqb + 1),
+        h_order(nqb);
+    std::vector<long long> h_pred(nqb), h_eff(nqb);
+    int64_t nnz = 0, npart = 0;
+
+    TRA_HIP(hipGetDevice(&m->device));
+    TRA_HIP(dev_alloc(&cls, (size_t)nqb * nkb));
+    TRA_HIP(dev_alloc(&cnt, (size_t)nqb * nkb));
+    TRA_HIP(dev_alloc(&row_blocks, nqb));
+    TRA_HIP(dev_alloc(&row_partial, nqb));
+    TRA_HIP(dev_alloc(&row_pred, nqb));
+    TRA_HIP(dev_alloc(&row_eff, nqb));
+    TRA_HIP(tra::launch_classify(d, nqb, nkb, cls, cnt, st));
+    TRA_HIP(tra::launch_row_stats(d, nqb, nkb, cls, cnt, row_blocks, row_partial, row_pred, row_eff, st));
+    TRA_HIP(hipMemcpyAsync(h_blocks.data(), row_blocks, nqb * sizeof(int32_t), hipMemcpyDeviceToHost, st));
+    TRA_HIP(hipMemcpyAsync(h_partial.data(), row_partial, nqb * sizeof(int32_t), hipMemcpyDeviceToHost, st));
+    TRA_HIP(hipMemcpyAsync(h_pred.data(), row_pred, nqb * sizeof(long long), hipMemcpyDeviceToHost, st));
+    TRA_HIP(hipMemcpyAsync(h_eff.data(), row_eff, nqb * sizeof(long long), hipMemcpyDeviceToHost, st));
+    TRA_HIP(hipStreamSynchronize(st));
+
+    h_row_ptr[0] = 0;
+    h_part_ptr[0] = 0;
+    for (int r = 0; r < nqb; ++r) {
+        nnz += h_blocks[r];
+        npart += h_partial[r];
+        if (nnz >= INT32_MAX) {
+            st_ = TRA_ERR_UNSUPPORTED;
+            goto fail;
+        }
+        h_row_ptr[r + 1] = (int32_t)nnz;
+        h_part_ptr[r + 1] = (int32_t)npart;
+    }
+    std::iota(h_order.begin(), h_order.end(), 0);
+    std::stable_sort(h_order.begin(), h_order.end(),
+                     [&](int x, int y) { return h_blocks[x] > h_blocks[y]; });
+
+    TRA_HIP(dev_alloc(&m->row_ptr, nqb + 1));
+    TRA_HIP(dev_alloc(&m->col_idx, (size_t)nnz));
+    TRA_HIP(dev_alloc(&m->emask_idx, (size_t)nnz));
+    TRA_HIP(dev_alloc(&m->emask, (size_t)npart * tra::kBlock * 4));
+    TRA_HIP(dev_alloc(&m->order, nqb));
+    TRA_HIP(dev_alloc(&m->bitmap, (size_t)nqb * words));
+    TRA_HIP(dev_alloc(&m->queue, 2));
+    TRA_HIP(dev_alloc(&part_ptr_d, nqb + 1));
+    TRA_HIP(dev_alloc(&part_list, (size_t)npart));
+    TRA_HIP(hipMemcpyAsync(m->row_ptr, h_row_ptr.data(), (nqb + 1) * sizeof(int32_t), hipMemcpyHostToDevice, st));
+    TRA_HIP(hipMemcpyAsync(part_ptr_d, h_part_ptr.data(), (nqb + 1) * sizeof(int32_t), hipMemcpyHostToDevice, st));
+    TRA_HIP(hipMemcpyAsync(m->order, h_order.data(), nqb * sizeof(int32_t), hipMemcpyHostToDevice, st));
+    TRA_HIP(hipMemsetAsync(m->queue, 0, 2 * sizeof(uint32_t), st));
+    TRA_HIP(tra::launch_compact(nqb, nkb, cls, m->row_ptr, part_ptr_d, m->col_idx, m->emask_idx, part_list, st));
+    TRA_HIP(tra::launch_fill_emask(d, (int)npart, part_list, nkb, m->emask, st));
+    TRA_HIP(tra::launch_bitmap(nqb, nkb, words, cls, m->bitmap, st));
+    TRA_HIP(hipStreamSynchronize(st));
+
+    {
+        tra_mask_info &in = m->info;
+        in.n = n;
+        in.f = f;
+        in.s = s;
+        in.nqb = nqb;
+        in.nkb = nkb;
+        in.kept_blocks = nnz;
+        in.partial_blocks = npart;
+        in.pred_elems = 0;
+        in.kept_elems = 0;
+        for (int r = 0; r < nqb; ++r) {
+            in.pred_elems += h_pred[r];
+            in.kept_elems += h_eff[r];
+        }
+        in.min_row_blocks = *std::min_element(h_blocks.begin(), h_blocks.end());
+        in.max_row_blocks = *std::max_element(h_blocks.begin(), h_blocks.end());
+        in.bitmap_words = words;
+        in.kind = kind;
+        in.granularity = p->granularity;
+    }
+    hipFree(cls);
+    hipFree(cnt);
+    hipFree(row_blocks);
+    hipFree(row_partial);
+    hipFree(row_pred);
+    hipFree(row_eff);
+    hipFree(part_ptr_d);
+    hipFree(part_list);
+    *out = m;
+    return TRA_OK;
+
+fail:
+    hipStreamSynchronize(st);
+    hipFree(cls);
+    hipFree(cnt);
+    hipFree(row_blocks);
+    hipFree(row_partial);
+    hipFree(row_pred);
+    hipFree(row_eff);
+    hipFree(part_ptr_d);
+    hipFree(part_list);
+    free_mask_buffers(m);
+    delete m;
+    return st_;
+}
+
+tra_status tra_mask_get_info(const tra_mask *m, tra_mask_info *out)
+{
+    if (m == nullptr || out == nullptr)
+        return TRA_ERR_INVALID;
+    *out = m->info;
+    return TRA_OK;
+}
+
+tra_status tra_mask_export(const tra_mask *m, uint32_t *bitmap, int32_t *row_ptr, int32_t *col_idx,
+                           int32_t *emask_idx, uint32_t *emask, int32_t *order)
+{
+    if (m == nullptr)
+        return TRA_ERR_INVALID;
+    const tra_mask_info &in = m->info;
+    tra_status st_ = TRA_OK;
+    if (bitmap)
+        TRA_HIP(hipMemcpy(bitmap, m->bitmap, (size_t)in.nqb * in.bitmap_words * sizeof(uint32_t), hipMemcpyDeviceToHost));
+    if (row_ptr)
+        TRA_HIP(hipMemcpy(row_ptr, m->row_ptr, (size_t)(in.nqb + 1) * sizeof(int32_t), hipMemcpyDeviceToHost));
+    if (col_idx && in.kept_blocks)
+        TRA_HIP(hipMemcpy(col_idx, m->col_idx, (size_t)in.kept_blocks * sizeof(int32_t), hipMemcpyDeviceToHost));
+    if (emask_idx && in.kept_blocks)
+        TRA_HIP(hipMemcpy(emask_idx, m->emask_idx, (size_t)in.kept_blocks * sizeof(int32_t), hipMemcpyDeviceToHost));
+    if (emask && in.partial_blocks)
+        TRA_HIP(hipMemcpy(emask, m->emask, (size_t)in.partial_blocks * tra::kBlock * 4 * sizeof(uint32_t), hipMemcpyDeviceToHost));
+    if (order)
+        TRA_HIP(hipMemcpy(order, m->order, (size_t)in.nqb * sizeof(int32_t), hipMemcpyDeviceToHost));
+    return TRA_OK;
+fail:
+    return st_;
+}
+
+void tra_mask_free(tra_mask *m)
+{
+    if (m == nullptr)
+        return;
+    free_mask_buffers(m);
+    delete m;
+}
+
+tra_status tra_sparse_attn_fwd(const tra_tensor *Q, const tra_tensor *K, const tra_tensor *V,
+                               const tra_mask *mask, tra_tensor *O, float *LSE, float scale,
+                               void *hip_stream)
+{
+    if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr || mask == nullptr)
+        return TRA_ERR_INVALID;
+    const tra_tensor *ts[4] = {Q, K, V, O};
+    const bool empty = Q->B == 0 || Q->H == 0;  // empty tensors may carry a NULL pointer
+    if (!empty && (!tensor_ok(Q) || !tensor_ok(K) || !tensor_ok(V) || !tensor_ok(O)))
+        return TRA_ERR_INVALID;
+    for (const tra_tensor *t : ts) {
+        if (t->B != Q->B || t->H != Q->H || t->N != Q->N || t->D != Q->D)
+            return TRA_ERR_SHAPE;
+        if (t->B < 0 || t->H < 0 || t->N < 0 || t->D < 0)
+            return TRA_ERR_SHAPE;
+    }
+    if (Q->N != mask->info.n)
+        return TRA_ERR_SHAPE;
+    for (const tra_tensor *t : ts)
+        if (t->dtype != Q->dtype)
+            return TRA_ERR_UNSUPPORTED;
+    if (Q->dtype != TRA_BF16 && Q->dtype != TRA_F32)
+        return TRA_ERR_UNSUPPORTED;
+    if (Q->D != 64 && Q->D != 128)
+        return TRA_ERR_UNSUPPORTED;
+    const int64_t vec = Q->dtype == TRA_BF16 ? 8 : 4;  // elements per 16-byte access
+    for (const tra_tensor *t : ts) {
+        if (t->stride[3] != 1)
+            return TRA_ERR_UNSUPPORTED;
+        for (int i = 0; i < 3; ++i)
+            if (t->stride[i] < 0 || t->stride[i] % vec != 0)
+                return TRA_ERR_UNSUPPORTED;
+        if (((uintptr_t)t->data) % 16 != 0)
+            return TRA_ERR_UNSUPPORTED;
+    }
+    if (empty)
+        return TRA_OK;
+    if (Q->B * Q->H * mask->info.nqb >= ((int64_t)1 << 31) || Q->B * Q->H * Q->N >= ((int64_t)1 << 40))
+        return TRA_ERR_UNSUPPORTED;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_status(e);
+    if (dev != mask->device)
+        return TRA_ERR_INVALID;
+
+    tra::AttnArgs a;
+    a.q = Q->data;
+    a.k = K->data;
+    a.v = V->data;
+    a.o = O->data;
+    a.lse = LSE;
+    for (int i = 0; i < 3; ++i) {
+        a.sq[i] = Q->stride[i];
+        a.sk[i] = K->stride[i];
+        a.sv[i] = V->stride[i];
+        a.so[i] = O->stride[i];
+    }
+    a.B = (int32_t)Q->B;
+    a.H = (int32_t)Q->H;
+    a.N = (int32_t)Q->N;
+    a.D = (int32_t)Q->D;
+    const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)Q->D);
+    a.scale_log2 = (float)(sc * 1.4426950408889634);
+    a.mask.row_ptr = mask->row_ptr;
+    a.mask.col_idx = mask->col_idx;
+    a.mask.emask_idx = mask->emask_idx;
+    a.mask.emask = mask->emask;
+    a.mask.order = mask->order;
+    a.mask.queue = mask->queue;
+    a.mask.nqb = (int32_t)mask->info.nqb;
+    hipStream_t st = (hipStream_t)hip_stream;
+    e = Q->dtype == TRA_BF16 ? tra::launch_attn_bf16(a, st) : tra::launch_attn_f32(a, st);
+    return hip_status(e);
+}
+
+}  // extern "C"

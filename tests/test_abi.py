@@ -1,0 +1,109 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+entry point, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tra.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import static_sparse_spatiotemporal_amd as tra
+    return tra.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tra_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert "tra_build_mask" in names and "tra_sparse_attn_fwd" in names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    for code, name in [(0, b"TRA_OK"), (-1, b"TRA_ERR_INVALID"), (-2, b"TRA_ERR_UNSUPPORTED"),
+                       (-3, b"TRA_ERR_SHAPE"), (-4, b"TRA_ERR_OOM"), (-5, b"TRA_ERR_HIP")]:
+        assert lib.tra_status_string(code) == name
+    assert lib.tra_status_string(42) == b"TRA_ERR_UNKNOWN"
+    assert lib.tra_version() >= 100
+    assert lib.tra_last_hip_error() == 0
+
+
+def _params(**kw):
+    import static_sparse_spatiotemporal_amd as tra
+    p = tra.MaskParams()
+    p.block = 128
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("f,s,kind,kw,expect", [
+    (0, 8, 1, {}, -1),                      # f < 1
+    (8, 0, 1, {}, -1),                      # s < 1
+    (8, 8, 9, {}, -1),                      # unknown kind
+    (8, 8, 1, {"granularity": 5}, -1),      # unknown granularity
+    (8, 8, 1, {"block": 64}, -2),           # only 128 x 128 blocks
+    (8, 8, 1, {"window": 3}, -1),           # field the family does not use
+    (8, 8, 1, {"r_s": 1}, -1),
+    (8, 8, 3, {}, -1),                      # SWA needs window >= 1
+    (8, 8, 3, {"window": -2}, -1),
+    (8, 12, 2, {"grid_h": 3, "grid_w": 5}, -3),   # s != grid_h * grid_w
+    (8, 12, 2, {"grid_h": 3, "grid_w": 4, "r_t": -1}, -1),
+    (8, 12, 2, {"grid_h": 0, "grid_w": 4}, -1),
+    (1 << 20, 1 << 12, 1, {}, -2),          # n >= 2^31
+])
+def test_build_mask_rejects_on_host(lib, f, s, kind, kw, expect):
+    out = ctypes.c_void_p(123)
+    p = _params(**kw)
+    st = lib.tra_build_mask(f, s, kind, ctypes.byref(p), None, ctypes.byref(out))
+    assert st == expect
+    assert out.value is None
+
+
+def test_build_mask_null_arguments(lib):
+    p = _params()
+    assert lib.tra_build_mask(8, 8, 1, ctypes.byref(p), None, None) == -1
+    out = ctypes.c_void_p()
+    assert lib.tra_build_mask(8, 8, 1, None, None, ctypes.byref(out)) == -1
+    p.reserved[3] = 1
+    assert lib.tra_build_mask(8, 8, 1, ctypes.byref(p), None, ctypes.byref(out)) == -1
+
+
+def test_null_handles(lib):
+    import static_sparse_spatiotemporal_amd as tra
+    info = tra.MaskInfo()
+    assert lib.tra_mask_get_info(None, ctypes.byref(info)) == -1
+    assert lib.tra_mask_export(None, None, None, None, None, None, None) == -1
+    lib.tra_mask_free(None)
+    t = tra.TensorDesc()
+    assert lib.tra_sparse_attn_fwd(None, None, None, None, None, None, 0.0, None) == -1
+    assert lib.tra_sparse_attn_fwd(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), None,
+                                   ctypes.byref(t), None, 0.0, None) == -1
+
+
+def test_oracle_and_product_are_independent():
+    """The product package never imports or includes the oracle, and the
+    oracle never imports or includes the product; only the workload
+    generators are shared."""
+    imp_oracle = re.compile(r"^\s*(import\s+oracle|from\s+oracle\b)|#\s*include\s*\"oracle\.h\"", re.M)
+    imp_prod = re.compile(r"^\s*(import|from)\s+static_sparse_spatiotemporal_amd\b|#\s*include\s*\"tra(_internal)?\.h\"", re.M)
+    pkg = os.path.join(ROOT, "static_sparse_spatiotemporal_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".cpp", ".hip", ".h")):
+                assert not imp_oracle.search(open(os.path.join(dirpath, fn)).read()), fn
+    for fn in os.listdir(os.path.join(ROOT, "oracle")):
+        if fn.endswith((".py", ".c", ".h")):
+            assert not imp_prod.search(open(os.path.join(ROOT, "oracle", fn)).read()), fn
+    wl = open(os.path.join(ROOT, "workloads", "__init__.py")).read()
+    assert not imp_oracle.search(wl) and not imp_prod.search(wl)

@@ -1,0 +1,231 @@
+"""GPU attention vs the fp64 oracle through the C ABI.
+
+Tolerances (max |O_gpu - O_oracle| over compared elements): 1e-4 for fp32
+inputs, 2e-2 for bf16 inputs with fp32 accumulation.  LSE: 1e-4 (fp32) and
+1e-3 (bf16 inputs).  The Q = 0 probe pins the mask the kernel applied: with
+every score 0 the softmax is uniform over the kept keys, so
+LSE = ln(#kept keys) and O = mean of V over them, at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import expected
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"f32": 1e-4, "bf16": 2e-2}
+TOL_LSE = {"f32": 1e-4, "bf16": 1e-3}
+
+
+@pytest.fixture(scope="module")
+def tra():
+    import static_sparse_spatiotemporal_amd as m
+    assert torch.cuda.is_available()
+    m.load_library()
+    return m
+
+
+def spec_of(w: workloads.Workload) -> oracle.MaskSpec:
+    return oracle.MaskSpec(w.kind, w.f, w.s, granularity=w.granularity, grid_h=w.grid_h,
+                           grid_w=w.grid_w, r_t=w.r_t, r_s=w.r_s, window=w.window)
+
+
+def build(tra, w):
+    return tra.build_mask(w.f, w.s, w.kind, **w.mask_kwargs())
+
+
+def run_and_compare(tra, w, q, k, v, rows=None, mask=None, block_keep=None, tag=""):
+    """Runs the kernel, then the oracle on `rows` (None = all), returns errors."""
+    print(f"[attn] {w.name}{tag} B={w.B} H={w.H} n={w.n} D={w.D} {w.dtype}", flush=True)
+    own = mask is None
+    if own:
+        mask = build(tra, w)
+    out, lse = tra.sparse_attn_fwd(q, k, v, mask)
+    torch.cuda.synchronize()
+    spec = spec_of(w)
+    if spec.granularity == "block_any" and block_keep is None:
+        block_keep = expected.cached_block_counts(spec) > 0
+    if rows is None:
+        ref_o, ref_l = oracle.attention_rows(*(workloads.to_oracle_array(x) for x in (q, k, v)), spec,
+                                             block_keep=block_keep)
+        got_o = out.float().cpu().numpy().reshape(-1, w.D)
+        got_l = lse.cpu().numpy().reshape(-1)
+    else:
+        # only the sampled heads travel to the host
+        heads = sorted(set((int(b), int(h)) for b, h, _ in rows))
+        index = {bh: i for i, bh in enumerate(heads)}
+        sel = lambda x: torch.stack([x[b, h] for b, h in heads])[None]
+        arrs = [workloads.to_oracle_array(sel(x)) for x in (q, k, v)]
+        sub_rows = np.array([(0, index[(int(b), int(h))], int(qq)) for b, h, qq in rows], dtype=np.int64)
+        ref_o, ref_l = oracle.attention_rows(*arrs, spec, rows=sub_rows, block_keep=block_keep)
+        bi, hi, qi = (torch.as_tensor(rows[:, i], device=out.device) for i in range(3))
+        got_o = out[bi, hi, qi].float().cpu().numpy()
+        got_l = lse[bi, hi, qi].cpu().numpy()
+    if own:
+        mask.free()
+    err_o = float(np.abs(got_o - ref_o).max())
+    err_l = float(np.abs(got_l - ref_l).max())
+    print(f"       max|dO|={err_o:.3e} max|dLSE|={err_l:.3e} rows={ref_o.shape[0]}", flush=True)
+    return err_o, err_l, out, lse
+
+
+SMALL = ["radial_f8_s64_fp32", "radius3d_t8_h16_w16"]
+LARGE = ["swa_f64_s256_w16", "radial_f20_s1536_block", "radial_f128_s1024_block"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_workload_full_parity(tra, name):
+    w = workloads.WORKLOADS[name]
+    q, k, v = workloads.make_qkv(w, device="cuda")
+    eo, el, _, _ = run_and_compare(tra, w, q, k, v)
+    assert eo <= TOL_O[w.dtype] and el <= TOL_LSE[w.dtype]
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_workload_sampled_parity(tra, name):
+    """Full-size inputs in the benchmark's launch configuration; the oracle
+    recomputes sampled rows one by one."""
+    w = workloads.WORKLOADS[name]
+    q, k, v = workloads.make_qkv(w, device="cuda")
+    rows = expected.sample_rows(w.n, w.B, w.H, heads_per_batch=2, blocks=4, seed=w.seed)
+    eo, el, _, _ = run_and_compare(tra, w, q, k, v, rows=rows)
+    assert eo <= TOL_O[w.dtype] and el <= TOL_LSE[w.dtype]
+
+
+@pytest.mark.parametrize("name", ["radius3d_t8_h16_w16", "swa_f64_s256_w16", "radial_f20_s1536_block",
+                                  "radial_f128_s1024_block"])
+def test_zero_query_probe(tra, name):
+    """Q = 0: LSE of every row must be ln(#kept keys of that row) (exact in
+    fp32 below 2^24 keys), O the mean of V over them (sampled rows)."""
+    w = workloads.WORKLOADS[name]
+    _, k, v = workloads.make_qkv(w, device="cuda")
+    q = torch.zeros_like(k)
+    spec = spec_of(w)
+    mask = build(tra, w)
+    out, lse = tra.sparse_attn_fwd(q, k, v, mask)
+    torch.cuda.synchronize()
+    print(f"[q0] {name}", flush=True)
+    if spec.granularity == "block_any":
+        counts, cls = expected.block_classes(spec, expected.cached_block_counts(spec))
+        kept = expected.kept_keys_per_row(spec, cls)
+    elif spec.kind == "swa":
+        i = np.arange(spec.n) // spec.s
+        kept = spec.s * (i - np.maximum(0, i - spec.window + 1) + 1)
+        for qq in (0, spec.n // 2 + 3, spec.n - 1):  # the closed form against the predicate
+            assert kept[qq] == sum(oracle.keep(spec, qq, t) for t in range(spec.n))
+    else:
+        kept = oracle.element_matrix(spec).sum(1)
+    want = np.log(kept.astype(np.float64))
+    got = lse.cpu().numpy().astype(np.float64)
+    err = float(np.abs(got - want[None, None, :]).max())
+    print(f"       max|dLSE| = {err:.3e}", flush=True)
+    assert err <= 1e-4
+    rows = expected.sample_rows(w.n, w.B, w.H, heads_per_batch=1, blocks=2, seed=7)
+    eo, _, _, _ = run_and_compare(tra, w, q, k, v, rows=rows, mask=mask, tag=" (Q=0)")
+    assert eo <= TOL_O[w.dtype]
+    mask.free()
+
+
+RAGGED = [
+    # (kind, f, s, granularity, extra, B, H, D, dtype)
+    ("radial", 10, 50, "element", {}, 1, 2, 64, "bf16"),
+    ("radial", 10, 50, "element", {}, 1, 2, 128, "bf16"),
+    ("radial", 10, 50, "element", {}, 1, 2, 64, "f32"),
+    ("radial", 300, 3, "element", {}, 1, 1, 64, "bf16"),
+    ("radial", 256, 1, "element", {}, 2, 1, 128, "bf16"),
+    ("radial", 7, 100, "block_any", {}, 1, 3, 128, "bf16"),
+    ("radial", 7, 100, "block_any", {}, 1, 2, 64, "f32"),
+    ("radial", 1, 200, "element", {}, 1, 2, 64, "bf16"),
+    ("radius3d", 3, 100, "element", dict(grid_h=10, grid_w=10, r_t=1, r_s=2), 2, 2, 64, "bf16"),
+    ("radius3d", 4, 128, "element", dict(grid_h=8, grid_w=16, r_t=0, r_s=0), 1, 2, 128, "bf16"),
+    ("swa", 9, 37, "element", dict(window=3), 1, 2, 128, "bf16"),
+    ("swa", 5, 128, "element", dict(window=1), 1, 2, 64, "f32"),
+    ("dense", 3, 100, "element", {}, 1, 2, 128, "bf16"),
+    ("dense", 4, 128, "block_any", {}, 1, 2, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: f"{c[0]}-f{c[1]}-s{c[2]}-{c[3]}-D{c[7]}-{c[8]}")
+def test_ragged_and_degenerate_full_parity(tra, case):
+    kind, f, s, gran, extra, B, H, D, dt = case
+    w = workloads.Workload(f"{kind}_f{f}_s{s}", kind, gran, f, s, B, H, D, dt, seed=4242 + f + s + D, **extra)
+    q, k, v = workloads.make_qkv(w, device="cuda")
+    eo, el, out, _ = run_and_compare(tra, w, q, k, v)
+    assert eo <= TOL_O[dt] and el <= TOL_LSE[dt]
+    if kind == "radius3d" and extra["r_t"] == 0 and extra["r_s"] == 0:
+        # the only key is the token itself: weight exactly 1, O == V bit for bit
+        assert torch.equal(out, v)
+
+
+def test_strided_views(tra):
+    """Q, K, V as [B, H, n, D] views of [B, n, H, D] storage (the layout a fused
+    QKV projection produces), output into a strided view as well."""
+    w = workloads.WORKLOADS["radius3d_t8_h16_w16"].replace(H=4)
+    q, k, v = workloads.make_qkv(w, device="cuda")
+    qs, ks, vs = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
+    assert not qs.is_contiguous()
+    mask = build(tra, w)
+    ref, ref_lse = tra.sparse_attn_fwd(q, k, v, mask)
+    out_store = torch.empty(w.B, w.n, w.H, w.D, dtype=q.dtype, device=q.device)
+    out = out_store.transpose(1, 2)
+    tra.sparse_attn_fwd(qs, ks, vs, mask, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    mask.free()
+
+
+def test_deterministic_and_reusable(tra):
+    """Every row is reduced by one workgroup in CSR order: results are bit
+    identical across calls, whatever the queue order.  The mask's work
+    counter resets itself, so back-to-back calls (also with other inputs) work."""
+    w = workloads.WORKLOADS["radial_f20_s1536_block"].replace(H=3)
+    q, k, v = workloads.make_qkv(w, device="cuda")
+    mask = build(tra, w)
+    o1, l1 = tra.sparse_attn_fwd(q, k, v, mask)
+    o2, l2 = tra.sparse_attn_fwd(q, k, v, mask)
+    q2, k2, v2 = workloads.make_qkv(w, device="cuda", seed=99)
+    o3, _ = tra.sparse_attn_fwd(q2, k2, v2, mask)
+    o4, l4 = tra.sparse_attn_fwd(q, k, v, mask)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o4) and torch.equal(l1, l4)
+    assert not torch.equal(o1, o3)
+    rows = expected.sample_rows(w.n, w.B, w.H, heads_per_batch=1, blocks=2, seed=5)
+    eo, el, _, _ = run_and_compare(tra, w, q2, k2, v2, rows=rows, mask=mask, tag=" (reuse)")
+    assert eo <= TOL_O["bf16"] and el <= TOL_LSE["bf16"]
+    mask.free()
+
+
+def test_empty_batch_is_a_no_op(tra):
+    w = workloads.WORKLOADS["radial_f8_s64_fp32"].replace(dtype="bf16")
+    mask = build(tra, w)
+    q = torch.zeros(0, 2, w.n, w.D, dtype=torch.bfloat16, device="cuda")
+    out, lse = tra.sparse_attn_fwd(q, q, q, mask)
+    assert out.shape == q.shape and lse.shape == (0, 2, w.n)
+    q = torch.zeros(1, 0, w.n, w.D, dtype=torch.bfloat16, device="cuda")
+    tra.sparse_attn_fwd(q, q, q, mask)
+    torch.cuda.synchronize()
+    mask.free()
+
+
+def test_errors_are_reported(tra):
+    w = workloads.WORKLOADS["radial_f8_s64_fp32"].replace(dtype="bf16")
+    mask = build(tra, w)
+    q, k, v = workloads.make_qkv(w, device="cuda")
+    with pytest.raises(tra.TraError, match="SHAPE"):
+        tra.sparse_attn_fwd(q[:, :, :256], k[:, :, :256], v[:, :, :256], mask)
+    with pytest.raises(tra.TraError, match="SHAPE"):
+        tra.sparse_attn_fwd(q, k[:, :, :, :32].contiguous(), v, mask)
+    with pytest.raises(tra.TraError, match="UNSUPPORTED"):
+        x = torch.zeros(1, 1, w.n, 96, dtype=torch.bfloat16, device="cuda")
+        tra.sparse_attn_fwd(x, x, x, mask)
+    with pytest.raises(tra.TraError, match="UNSUPPORTED"):
+        tra.sparse_attn_fwd(q, k.float(), v, mask)
+    with pytest.raises(tra.TraError, match="UNSUPPORTED"):
+        big = torch.zeros(1, 1, w.n, 68, dtype=torch.bfloat16, device="cuda")[..., :64]
+        tra.sparse_attn_fwd(big, k, v, mask)  # row pitch 68 is not a multiple of 8
+    with pytest.raises(tra.TraError, match="SHAPE"):
+        tra.build_mask(8, 12, "radius3d", grid_h=3, grid_w=5)
+    mask.free()

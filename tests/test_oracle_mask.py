@@ -273,3 +273,10 @@ def test_block_any_contains_element_mask():
     keep = oracle.block_counts(spec) > 0
     dil = np.kron(keep.astype(np.uint8), np.ones((128, 128), np.uint8))[:spec.n, :spec.n]
     assert not (elem.astype(bool) & ~dil.astype(bool)).any()
+
+
+def test_block_counts_rows_subset():
+    spec = MaskSpec("radial", 11, 40, block=128)
+    full = oracle.block_counts(spec)
+    rows = np.array([3, 0, 2], dtype=np.int64)
+    np.testing.assert_array_equal(oracle.block_counts_rows(spec, rows, threads=2), full[rows])
