@@ -73,7 +73,7 @@ def cpu_baseline(w, q, k, v, mask_info, target_s: float):
     rng = np.random.default_rng(w.seed)
     nb = spec.nb
     heads = [(0, 0), (0, w.H - 1)] if w.H > 1 else [(0, 0)]
-    qblocks = sorted(set(rng.choice(nb, size=min(nb, 32), replace=False).tolist()))
+    qblocks = sorted(set(rng.choice(nb, size=min(nb, 128), replace=False).tolist()))
     block_keep = None
     if spec.granularity == "block_any":
         counts = oracle.block_counts_rows(spec, qblocks, threads)

@@ -103,6 +103,9 @@ typedef struct {
     int64_t pred_elems;     /* pairs kept by the family's element predicate */
     int64_t min_row_blocks, max_row_blocks;
     int64_t bitmap_words;   /* uint32 words per bitmap row = ceil(nkb / 32) */
+    int64_t work_items;     /* bf16 kernel work items per (b, h): query blocks
+                               paired by key-block overlap, plus singles     */
+    int64_t tile_loads;     /* K/V tiles the bf16 kernel loads per (b, h)    */
     int32_t kind, granularity;
 } tra_mask_info;
 
@@ -174,8 +177,10 @@ tra_status tra_mask_get_info(const tra_mask *mask, tra_mask_info *out);
  *             its bitmask (partial blocks numbered in CSR order)
  *   emask     uint32[partial_blocks * 128 * 4]; row r of a partial block is
  *             4 words, bit b of word w = key (w * 32 + b) of the block kept
- *   order     int32[nqb]; query blocks by decreasing kept-block count
- *             (ties by index), the order the attention kernel takes them
+ *   order     int32[nqb]; the query blocks in chunks of 64 consecutive
+ *             blocks, each chunk ordered by decreasing kept-block count
+ *             (ties by index): the order in which the attention kernels
+ *             take the blocks of one chunk
  */
 tra_status tra_mask_export(const tra_mask *mask, uint32_t *bitmap, int32_t *row_ptr,
                            int32_t *col_idx, int32_t *emask_idx, uint32_t *emask, int32_t *order);

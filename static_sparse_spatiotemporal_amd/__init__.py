@@ -55,7 +55,8 @@ class MaskInfo(ctypes.Structure):
                 ("kept_blocks", ctypes.c_int64), ("partial_blocks", ctypes.c_int64),
                 ("kept_elems", ctypes.c_int64), ("pred_elems", ctypes.c_int64),
                 ("min_row_blocks", ctypes.c_int64), ("max_row_blocks", ctypes.c_int64),
-                ("bitmap_words", ctypes.c_int64), ("kind", ctypes.c_int32),
+                ("bitmap_words", ctypes.c_int64), ("work_items", ctypes.c_int64),
+                ("tile_loads", ctypes.c_int64), ("kind", ctypes.c_int32),
                 ("granularity", ctypes.c_int32)]
 
 

@@ -2,35 +2,40 @@
 // fp32 accumulation.
 //
 // Computes O = softmax((Q K^T + M) * scale) V (Radial Attention section 2,
-// eq. 2) for one 128-query block at a time over the kept 128-key blocks of
-// its CSR row, with the streaming softmax: running row maximum m and
-// denominator l, the accumulator rescaled by 2^(m_old - m_new) when the
-// maximum grows.  Scores are multiplied by scale * log2(e) so that exp is
-// v_exp_f32 (base 2).
+// eq. 2) over the kept 128 x 128 blocks of the static mask, with the
+// streaming softmax: running row maximum m and denominator l, the
+// accumulator rescaled by 2^(m_old - m_new) when the maximum grows.  Scores
+// are multiplied by scale * log2(e) so that exp is v_exp_f32 (base 2).
 //
-// Mapping (one workgroup = 4 wave64s = one 128-query block; two workgroups
-// per CU, i.e. two waves per SIMD, so one wave's softmax can run while the
-// other wave's matrix products occupy the MFMA unit):
-//   - wave w owns queries 32w .. 32w+31; its Q fragments stay in registers;
+// Mapping.  One workgroup = 8 wave64s (two per SIMD) = one work item of the
+// mask's pair schedule: two 128-query blocks whose kept key blocks largely
+// coincide (for the radial mask: the same in-frame position in adjacent
+// frames), walked over the union of their key blocks.  Waves 0-3 own the
+// first query block, waves 4-7 the second; each wave owns 32 queries.  Every
+// K/V tile loaded into LDS thus serves up to 256 queries.
+//   - K and V tiles (128 x D bf16) are double-buffered in LDS (128 KB at
+//     D = 128) and copied HBM -> LDS by global_load_lds_dwordx4 (no register
+//     staging).  The copy of tile u + 1 is issued right after the single
+//     barrier of tile u, so it has a whole tile of compute to land.  An XOR
+//     swizzle of 16-byte chunks keeps the operand reads free of bank
+//     conflicts;
 //   - scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: a lane holds one query and 64 of the 128 keys
 //     of the tile, so the row max is lane-local plus one permlane32 swap, and
 //     the row sum stays lane-local until the epilogue;
 //   - the output is accumulated transposed, O^T += V^T P^T: the probabilities
-//     are already the B operand (keys permuted inside each 16-key step in
-//     the same way on both operands), and V^T comes from the row-major V
-//     tile through ds_read_b64_tr_b16;
-//   - K and V tiles (128 x D bf16, 64 KB per workgroup at D = 128) are copied
-//     HBM -> LDS by global_load_lds_dwordx4 (no register staging) with an XOR
-//     swizzle of 16-byte chunks that keeps the K operand reads and the
-//     transposing V reads free of bank conflicts.  The next K tile streams in
-//     during softmax and P V, the next V tile during the next Q K^T;
+//     are already the B operand (keys permuted inside each 16-key step in the
+//     same way on both operands), and V^T comes from the row-major V tile
+//     through ds_read_b64_tr_b16;
+//   - operand fragments are read one step ahead of the MFMAs that use them;
 //   - the accumulator is rescaled only when some row's maximum grows by more
 //     than 2^8 (wave-uniform test); otherwise the stale maximum is kept, which
 //     leaves probabilities <= 2^8 and the result exact up to rounding;
-//   - partly kept tiles get their element bitmask applied to the scores;
-//   - workgroups are persistent and pop (batch * head, query block) items
-//     from a device counter in the mask's heaviest-first order.
+//   - partly kept tiles get their element bitmask applied to the scores; the
+//     waves of a query block that does not keep a tile of the union skip it;
+//   - workgroups are persistent and pop items from per-XCD queues of chunks
+//     of neighbouring items (see WorkQueue), so that the workgroups sharing
+//     an L2 stream largely the same K/V tiles.
 #include "attn_common.h"
 
 namespace tra {
@@ -38,17 +43,23 @@ namespace {
 
 #define LDS_AS __attribute__((address_space(3)))
 
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+
 template <int D>
 struct Geo {
-    static constexpr int ROWB = D * 2;      // bytes per K/V row
-    static constexpr int CPR = D / 8;       // 16-byte chunks per row
-    static constexpr int RPI = 64 / CPR;    // rows per 1 KB copy instruction
-    static constexpr int NCOPY = CPR / 2;   // copy instructions per thread per tile
-    static constexpr int NKS = D / 16;      // k-steps of Q K^T
-    static constexpr int NDB = D / 32;      // 32-row blocks of O^T
+    static constexpr int ROWB = D * 2;                  // bytes per K/V row
+    static constexpr int TILE = kBlock * ROWB;          // bytes per K or V tile
+    static constexpr int CPR = D / 8;                   // 16-byte chunks per row
+    static constexpr int RPI = 64 / CPR;                // rows per 1 KB copy instruction
+    static constexpr int NCOPY = kBlock * CPR / kThreads;  // copies per thread per tile
+    static constexpr int NKS = D / 16;                  // k-steps of Q K^T
+    static constexpr int NDB = D / 32;                  // 32-row blocks of O^T
 };
 
-// Physical chunk = logical chunk XOR swizzle(row).
+// Physical chunk = logical chunk XOR swizzle(row).  K rows are read 16 at a
+// time at one chunk column (S^T A operand); V rows 4 at a time, 64
+// contiguous bytes each (ds_read_b64_tr_b16 for the V^T A operand).
 template <int D>
 __device__ inline int k_swz(int row)
 {
@@ -62,31 +73,40 @@ __device__ inline int v_swz(int row)
 
 __device__ inline void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Copy one 128-row tile of X (rows key0 ..) into LDS; rows past N repeat row
+// Copy one 128-row tile of X (rows key0 ..) into LDS.  Copy instruction i of
+// wave w fills bytes (8 i + w) KB .. of the tile: rows crow0 + 8 RPI i, where
+// crow0 = w RPI + lane / CPR.  `lane_off` is this lane's element offset
+// inside the tile (row crow0, swizzled column `col`).  Rows past N repeat row
 // N - 1 (their scores are masked, so only finiteness matters).
 template <int D>
 __device__ inline void copy_tile(const __bf16 *X, int64_t stride, int key0, int N, char LDS_AS *dst,
-                                 int wave, int row0, int col)
+                                 int wave, int crow0, int col, int64_t lane_off)
 {
     using G = Geo<D>;
-    const bool whole = key0 + 128 <= N;
+    const __bf16 *tile = X + (int64_t)key0 * stride;  // wave-uniform
+    if (key0 + kBlock <= N) {
 #pragma unroll
-    for (int i = 0; i < G::NCOPY; ++i) {
-        int r = key0 + row0 + 4 * G::RPI * i;
-        if (!whole)
-            r = r < N ? r : N - 1;
-        const __bf16 *src = X + (int64_t)r * stride + col;
-        __builtin_amdgcn_global_load_lds((const void *)src, (void LDS_AS *)(dst + (4 * i + wave) * 1024), 16, 0, 0);
+        for (int i = 0; i < G::NCOPY; ++i)
+            __builtin_amdgcn_global_load_lds((const void *)(tile + lane_off + i * (8 * G::RPI) * stride),
+                                             (void LDS_AS *)(dst + (8 * i + wave) * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < G::NCOPY; ++i) {
+            int r = key0 + crow0 + 8 * G::RPI * i;
+            r = (r < N ? r : N - 1) - key0;
+            __builtin_amdgcn_global_load_lds((const void *)(tile + (int64_t)r * stride + col),
+                                             (void LDS_AS *)(dst + (8 * i + wave) * 1024), 16, 0, 0);
+        }
     }
 }
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(AttnArgs a)
 {
     using G = Geo<D>;
-    __shared__ __attribute__((aligned(1024))) char sK[kBlock * G::ROWB];
-    __shared__ __attribute__((aligned(1024))) char sV[kBlock * G::ROWB];
+    __shared__ __attribute__((aligned(1024))) char sK[2 * G::TILE];
+    __shared__ __attribute__((aligned(1024))) char sV[2 * G::TILE];
     __shared__ int sItem;
     char LDS_AS *lK = (char LDS_AS *)sK;
     char LDS_AS *lV = (char LDS_AS *)sV;
@@ -94,8 +114,9 @@ void attn_fwd_bf16(AttnArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = wave >> 2, w4 = wave & 3;
     const int lq = lane & 31, hh = lane >> 5;
-    const int N = a.N, nqb = a.mask.nqb, total = a.B * a.H * nqb;
+    const int N = a.N;
     const float c2 = a.scale_log2;
     constexpr float kTau = 8.f;
 
@@ -114,32 +135,40 @@ void attn_fwd_bf16(AttnArgs a)
             voff[db] = keyA * G::ROWB + (((d >> 3) ^ v_swz<D>(keyA)) << 4) + ((d & 7) << 1);
         }
     }
-    // Copy geometry: row of this lane in copy instruction 0, logical column.
+    // Copy geometry (see copy_tile).
     const int crow0 = wave * G::RPI + lane / G::CPR;
     const int cpc = lane % G::CPR;
     const int colK = (cpc ^ k_swz<D>(crow0)) * 8;
     const int colV = (cpc ^ v_swz<D>(crow0)) * 8;
+    const int64_t offK = crow0 * a.sk[2] + colK;
+    const int64_t offV = crow0 * a.sv[2] + colV;
+    // The schedule is read-only for the whole launch: read it through the
+    // constant address space so that the loads are scalar.
+    typedef const __attribute__((address_space(4))) int32_t cint;
+    cint *pair_rows = (cint *)a.mask.pair_rows;
+    cint *pair_ptr = (cint *)a.mask.pair_ptr;
+    cint *u_col = (cint *)a.mask.u_col;
+    cint *u_em = (cint *)a.mask.u_em;
 
-    for (;;) {
-        const int item = pop_item(a.mask.queue, &sItem);
-        if (item >= total)
-            break;
-        const int bh = item / nqb;
-        const int row = a.mask.order[item - bh * nqb];
+    WorkQueue wq(a.mask.queue, a.mask.pair_order, a.mask.npairs, kPairChunk, a.B * a.H);
+    int wx = xcd_id(), wtries = 0, bh = 0, pair = 0;
+    while (wq.next(wx, wtries, &sItem, bh, pair)) {
+        const int row = pair_rows[2 * pair + half];  // -1: this half idles
+        const bool active = row >= 0;
+        const int u0 = pair_ptr[pair], u1 = pair_ptr[pair + 1];
         const int b = bh / a.H, h = bh - b * a.H;
         const __bf16 *Qp = (const __bf16 *)a.q + b * a.sq[0] + h * a.sq[1];
         const __bf16 *Kp = (const __bf16 *)a.k + b * a.sk[0] + h * a.sk[1];
         const __bf16 *Vp = (const __bf16 *)a.v + b * a.sv[0] + h * a.sv[1];
         __bf16 *Op = (__bf16 *)a.o + b * a.so[0] + h * a.so[1];
-        const int q0 = row * kBlock + wave * 32;
-        const int e0 = a.mask.row_ptr[row], e1 = a.mask.row_ptr[row + 1];
+        const int q0 = row * kBlock + w4 * 32;
 
-        if (e0 < e1) {
-            copy_tile<D>(Kp, a.sk[2], a.mask.col_idx[e0] * kBlock, N, lK, wave, crow0, colK);
-            copy_tile<D>(Vp, a.sv[2], a.mask.col_idx[e0] * kBlock, N, lV, wave, crow0, colV);
+        if (u0 < u1) {
+            copy_tile<D>(Kp, a.sk[2], u_col[u0] * kBlock, N, lK, wave, crow0, colK, offK);
+            copy_tile<D>(Vp, a.sv[2], u_col[u0] * kBlock, N, lV, wave, crow0, colV, offV);
         }
         bf16x8 qf[G::NKS];
-        {
+        if (active) {
             const int qr = q0 + lq < N ? q0 + lq : N - 1;
 #pragma unroll
             for (int ks = 0; ks < G::NKS; ++ks)
@@ -150,32 +179,50 @@ void attn_fwd_bf16(AttnArgs a)
         for (int db = 0; db < G::NDB; ++db)
             o[db] = f32x16{};
         float m = kNegInf, l = 0.f;
-        wait_copies();
-        __syncthreads();
 
-        for (int e = e0; e < e1; ++e) {
-            const int em = a.mask.emask_idx[e];
+        for (int u = u0; u < u1; ++u) {
+            const int buf = (u - u0) & 1;
+            // Tile u has landed everywhere and every wave is done with tile
+            // u - 1, whose buffer now receives tile u + 1.
+            wait_copies();
+            __syncthreads();
+            if (u + 1 < u1) {
+                const int nb = buf ^ 1;
+                copy_tile<D>(Kp, a.sk[2], u_col[u + 1] * kBlock, N, lK + nb * G::TILE, wave, crow0, colK, offK);
+                copy_tile<D>(Vp, a.sv[2], u_col[u + 1] * kBlock, N, lV + nb * G::TILE, wave, crow0, colV, offV);
+            }
+            const int em = active ? u_em[2 * u + half] : kAbsent;
+            if (em == kAbsent)
+                continue;
+            const char LDS_AS *tK = lK + buf * G::TILE;
+            const char LDS_AS *tV = lV + buf * G::TILE;
+
             // ---- S^T = K Q^T: 128 keys x 32 queries ----
             f32x16 s[4];
 #pragma unroll
             for (int kb4 = 0; kb4 < 4; ++kb4)
                 s[kb4] = f32x16{};
+            bf16x8 kf[2][4];
 #pragma unroll
-            for (int ks = 0; ks < G::NKS; ++ks)
+            for (int kb4 = 0; kb4 < 4; ++kb4)
+                kf[0][kb4] = *(const bf16x8 LDS_AS *)(tK + koff[0] + kb4 * 32 * G::ROWB);
 #pragma unroll
-                for (int kb4 = 0; kb4 < 4; ++kb4) {
-                    const bf16x8 kf = *(const bf16x8 LDS_AS *)(lK + koff[ks] + kb4 * 32 * G::ROWB);
-                    s[kb4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb4], 0, 0, 0);
+            for (int ks = 0; ks < G::NKS; ++ks) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (ks + 1 < G::NKS) {
+#pragma unroll
+                    for (int kb4 = 0; kb4 < 4; ++kb4)
+                        kf[(ks + 1) & 1][kb4] = *(const bf16x8 LDS_AS *)(tK + koff[ks + 1] + kb4 * 32 * G::ROWB);
                 }
-            // V(e) has landed and every wave is done with K(e): stream K(e+1).
-            wait_copies();
-            __syncthreads();
-            if (e + 1 < e1)
-                copy_tile<D>(Kp, a.sk[2], a.mask.col_idx[e + 1] * kBlock, N, lK, wave, crow0, colK);
+#pragma unroll
+                for (int kb4 = 0; kb4 < 4; ++kb4)
+                    s[kb4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks & 1][kb4], qf[ks], s[kb4], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 
             // ---- element mask of a partly kept tile ----
             if (em >= 0) {
-                const uint4 mw = ((const uint4 *)a.mask.emask)[(size_t)em * kBlock + wave * 32 + lq];
+                const uint4 mw = ((const uint4 *)a.mask.emask)[(size_t)em * kBlock + w4 * 32 + lq];
                 const uint32_t words[4] = {mw.x, mw.y, mw.z, mw.w};
 #pragma unroll
                 for (int kb4 = 0; kb4 < 4; ++kb4)
@@ -221,43 +268,52 @@ void attn_fwd_bf16(AttnArgs a)
             l += ls[0] + ls[1];
 
             // ---- O^T += V^T P^T ----
+            auto read_v = [&](int t, int db) {
+                const char LDS_AS *pa = tV + voff[db] + t * 16 * G::ROWB;
+                const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)pa);
+                const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(pa + 8 * G::ROWB));
+                return __builtin_shufflevector(__builtin_bit_cast(bf16x4, va), __builtin_bit_cast(bf16x4, vb),
+                                               0, 1, 2, 3, 4, 5, 6, 7);
+            };
+            bf16x8 vf[2][G::NDB];
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
+            for (int db = 0; db < G::NDB; ++db)
+                vf[0][db] = read_v(0, db);
 #pragma unroll
-                for (int db = 0; db < G::NDB; ++db) {
-                    const char LDS_AS *pa = lV + voff[db] + t * 16 * G::ROWB;
-                    const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)pa);
-                    const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(pa + 8 * G::ROWB));
-                    const bf16x8 vf = __builtin_shufflevector(__builtin_bit_cast(bf16x4, va),
-                                                              __builtin_bit_cast(bf16x4, vb),
-                                                              0, 1, 2, 3, 4, 5, 6, 7);
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t], o[db], 0, 0, 0);
+            for (int t = 0; t < 8; ++t) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (t + 1 < 8) {
+#pragma unroll
+                    for (int db = 0; db < G::NDB; ++db)
+                        vf[(t + 1) & 1][db] = read_v(t + 1, db);
                 }
-            // K(e+1) has landed and every wave is done with V(e): stream V(e+1).
-            wait_copies();
-            __syncthreads();
-            if (e + 1 < e1)
-                copy_tile<D>(Vp, a.sv[2], a.mask.col_idx[e + 1] * kBlock, N, lV, wave, crow0, colV);
+#pragma unroll
+                for (int db = 0; db < G::NDB; ++db)
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t & 1][db], pf[t], o[db], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l) ----
-        const float lt = lane_pair_sum(l);
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        const int q = q0 + lq;
-        if (q < N) {
-            __bf16 *orow = Op + (int64_t)q * a.so[2];
+        if (active) {
+            const float lt = lane_pair_sum(l);
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            const int q = q0 + lq;
+            if (q < N) {
+                __bf16 *orow = Op + (int64_t)q * a.so[2];
 #pragma unroll
-            for (int db = 0; db < G::NDB; ++db)
+                for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    f32x4 v;
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                        f32x4 v;
 #pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        v[x] = o[db][4 * i4 + x] * inv;
-                    *(bf16x4 *)(orow + db * 32 + 8 * i4 + 4 * hh) = __builtin_convertvector(v, bf16x4);
-                }
-            if (a.lse && hh == 0)
-                a.lse[(int64_t)bh * N + q] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+                        for (int x = 0; x < 4; ++x)
+                            v[x] = o[db][4 * i4 + x] * inv;
+                        *(bf16x4 *)(orow + db * 32 + 8 * i4 + 4 * hh) = __builtin_convertvector(v, bf16x4);
+                    }
+                if (a.lse && hh == 0)
+                    a.lse[(int64_t)bh * N + q] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+            }
         }
     }
     retire_group(a.mask.queue);
@@ -267,8 +323,9 @@ void attn_fwd_bf16(AttnArgs a)
 
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t st)
 {
-    return a.D == 128 ? launch_persistent(attn_fwd_bf16<128>, 256, a, st)
-                      : launch_persistent(attn_fwd_bf16<64>, 256, a, st);
+    const long long items = (long long)a.B * a.H * a.mask.npairs;
+    return a.D == 128 ? launch_persistent(attn_fwd_bf16<128>, kThreads, items, a, st)
+                      : launch_persistent(attn_fwd_bf16<64>, kThreads, items, a, st);
 }
 
 }  // namespace tra

@@ -18,16 +18,11 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(AttnArgs a)
     __shared__ int sItem;
     const int tid = threadIdx.x;
     const int N = a.N;
-    const int nqb = a.mask.nqb;
-    const int total = a.B * a.H * nqb;
     const float c2 = a.scale_log2;
 
-    for (;;) {
-        const int item = pop_item(a.mask.queue, &sItem);
-        if (item >= total)
-            break;
-        const int bh = item / nqb;
-        const int row = a.mask.order[item - bh * nqb];
+    WorkQueue wq(a.mask.queue, a.mask.order, a.mask.nqb, kChunk, a.B * a.H);
+    int wx = xcd_id(), wtries = 0, bh = 0, row = 0;
+    while (wq.next(wx, wtries, &sItem, bh, row)) {
         const int b = bh / a.H, h = bh - b * a.H;
         const float *Qp = (const float *)a.q + b * a.sq[0] + h * a.sq[1];
         const float *Kp = (const float *)a.k + b * a.sk[0] + h * a.sk[1];
@@ -114,8 +109,9 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(AttnArgs a)
 
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t st)
 {
-    return a.D == 128 ? launch_persistent(attn_fwd_f32<128>, 128, a, st)
-                      : launch_persistent(attn_fwd_f32<64>, 128, a, st);
+    const long long items = (long long)a.B * a.H * a.mask.nqb;
+    return a.D == 128 ? launch_persistent(attn_fwd_f32<128>, 128, items, a, st)
+                      : launch_persistent(attn_fwd_f32<64>, 128, items, a, st);
 }
 
 }  // namespace tra

@@ -37,6 +37,88 @@ hipError_t dev_alloc(T **p, size_t count)
     return hipMalloc((void **)p, std::max<size_t>(count, 1) * sizeof(T));
 }
 
+// |A n B| / |A u B| of two ascending lists (1 for two empty lists).
+double jaccard(const int32_t *a, int na, const int32_t *b, int nb)
+{
+    int i = 0, j = 0, inter = 0;
+    while (i < na && j < nb) {
+        if (a[i] == b[j]) {
+            ++inter;
+            ++i;
+            ++j;
+        } else if (a[i] < b[j]) {
+            ++i;
+        } else {
+            ++j;
+        }
+    }
+    const int uni = na + nb - inter;
+    return uni ? (double)inter / uni : 1.0;
+}
+
+// Host side of the pair schedule (see MaskDev): greedy pairing of query
+// blocks, in order, with the unpaired partner among r + 1 and r + s / 128
+// (same position in the next frame) that shares the most key blocks, if the
+// Jaccard overlap exceeds 1/2; then the merged key-block list of each pair.
+struct PairSchedule {
+    std::vector<int32_t> rows, ptr, col, em, order;
+};
+
+PairSchedule build_pairs(int nqb, int64_t s, const std::vector<int32_t> &row_ptr,
+                         const std::vector<int32_t> &col_idx, const std::vector<int32_t> &emask_idx)
+{
+    PairSchedule ps;
+    std::vector<int> offs = {1};
+    if (s % tra::kBlock == 0 && s / tra::kBlock > 1)
+        offs.push_back((int)(s / tra::kBlock));
+    std::vector<char> used(nqb, 0);
+    auto list = [&](int r) { return col_idx.data() + row_ptr[r]; };
+    auto len = [&](int r) { return row_ptr[r + 1] - row_ptr[r]; };
+    for (int r = 0; r < nqb; ++r) {
+        if (used[r])
+            continue;
+        int best = -1;
+        double bj = 0.5;
+        for (int off : offs) {
+            const int r2 = r + off;
+            if (r2 >= nqb || used[r2])
+                continue;
+            const double j = jaccard(list(r), len(r), list(r2), len(r2));
+            if (j > bj) {
+                bj = j;
+                best = r2;
+            }
+        }
+        used[r] = 1;
+        if (best >= 0)
+            used[best] = 1;
+        ps.rows.push_back(r);
+        ps.rows.push_back(best);
+    }
+    const int np = (int)ps.rows.size() / 2;
+    ps.ptr.assign(np + 1, 0);
+    for (int p = 0; p < np; ++p) {
+        const int a = ps.rows[2 * p], b = ps.rows[2 * p + 1];
+        int i = row_ptr[a], ie = row_ptr[a + 1];
+        int j = b >= 0 ? row_ptr[b] : 0, je = b >= 0 ? row_ptr[b + 1] : 0;
+        while (i < ie || j < je) {
+            const int ca = i < ie ? col_idx[i] : INT32_MAX;
+            const int cb = j < je ? col_idx[j] : INT32_MAX;
+            const int c = ca < cb ? ca : cb;
+            ps.col.push_back(c);
+            ps.em.push_back(ca == c ? emask_idx[i++] : tra::kAbsent);
+            ps.em.push_back(cb == c ? emask_idx[j++] : tra::kAbsent);
+        }
+        ps.ptr[p + 1] = (int32_t)ps.col.size();
+    }
+    ps.order.resize(np);
+    std::iota(ps.order.begin(), ps.order.end(), 0);
+    for (int c0 = 0; c0 < np; c0 += tra::kPairChunk)
+        std::stable_sort(ps.order.begin() + c0, ps.order.begin() + std::min(np, c0 + tra::kPairChunk),
+                         [&](int x, int y) { return ps.ptr[x + 1] - ps.ptr[x] > ps.ptr[y + 1] - ps.ptr[y]; });
+    return ps;
+}
+
 void free_mask_buffers(tra_mask *m)
 {
     hipFree(m->bitmap);
@@ -45,6 +127,11 @@ void free_mask_buffers(tra_mask *m)
     hipFree(m->emask_idx);
     hipFree(m->emask);
     hipFree(m->order);
+    hipFree(m->pair_rows);
+    hipFree(m->pair_ptr);
+    hipFree(m->u_col);
+    hipFree(m->u_em);
+    hipFree(m->pair_order);
     hipFree(m->queue);
 }
 
@@ -141,6 +228,8 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
     std::vector<int32_t> h_blocks(nqb), h_partial(nqb), h_row_ptr(nqb + 1), h_part_ptr(nqb + 1),
         h_order(nqb);
     std::vector<long long> h_pred(nqb), h_eff(nqb);
+    std::vector<int32_t> h_col, h_em;
+    PairSchedule ps;
     int64_t nnz = 0, npart = 0;
 
     TRA_HIP(hipGetDevice(&m->device));
@@ -170,9 +259,11 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
         h_row_ptr[r + 1] = (int32_t)nnz;
         h_part_ptr[r + 1] = (int32_t)npart;
     }
+    // Within each chunk of kChunk consecutive query blocks, heaviest first.
     std::iota(h_order.begin(), h_order.end(), 0);
-    std::stable_sort(h_order.begin(), h_order.end(),
-                     [&](int x, int y) { return h_blocks[x] > h_blocks[y]; });
+    for (int c0 = 0; c0 < nqb; c0 += tra::kChunk)
+        std::stable_sort(h_order.begin() + c0, h_order.begin() + std::min(nqb, c0 + tra::kChunk),
+                         [&](int x, int y) { return h_blocks[x] > h_blocks[y]; });
 
     TRA_HIP(dev_alloc(&m->row_ptr, nqb + 1));
     TRA_HIP(dev_alloc(&m->col_idx, (size_t)nnz));
@@ -180,17 +271,39 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
     TRA_HIP(dev_alloc(&m->emask, (size_t)npart * tra::kBlock * 4));
     TRA_HIP(dev_alloc(&m->order, nqb));
     TRA_HIP(dev_alloc(&m->bitmap, (size_t)nqb * words));
-    TRA_HIP(dev_alloc(&m->queue, 2));
+    TRA_HIP(dev_alloc(&m->queue, tra::kQueueWords));
     TRA_HIP(dev_alloc(&part_ptr_d, nqb + 1));
     TRA_HIP(dev_alloc(&part_list, (size_t)npart));
     TRA_HIP(hipMemcpyAsync(m->row_ptr, h_row_ptr.data(), (nqb + 1) * sizeof(int32_t), hipMemcpyHostToDevice, st));
     TRA_HIP(hipMemcpyAsync(part_ptr_d, h_part_ptr.data(), (nqb + 1) * sizeof(int32_t), hipMemcpyHostToDevice, st));
     TRA_HIP(hipMemcpyAsync(m->order, h_order.data(), nqb * sizeof(int32_t), hipMemcpyHostToDevice, st));
-    TRA_HIP(hipMemsetAsync(m->queue, 0, 2 * sizeof(uint32_t), st));
+    TRA_HIP(hipMemsetAsync(m->queue, 0, tra::kQueueWords * sizeof(uint32_t), st));
     TRA_HIP(tra::launch_compact(nqb, nkb, cls, m->row_ptr, part_ptr_d, m->col_idx, m->emask_idx, part_list, st));
     TRA_HIP(tra::launch_fill_emask(d, (int)npart, part_list, nkb, m->emask, st));
     TRA_HIP(tra::launch_bitmap(nqb, nkb, words, cls, m->bitmap, st));
     TRA_HIP(hipStreamSynchronize(st));
+
+    // Pair schedule for the bf16 kernel, from the finished CSR.
+    h_col.resize(nnz);
+    h_em.resize(nnz);
+    if (nnz) {
+        TRA_HIP(hipMemcpy(h_col.data(), m->col_idx, nnz * sizeof(int32_t), hipMemcpyDeviceToHost));
+        TRA_HIP(hipMemcpy(h_em.data(), m->emask_idx, nnz * sizeof(int32_t), hipMemcpyDeviceToHost));
+    }
+    ps = build_pairs(nqb, s, h_row_ptr, h_col, h_em);
+    m->npairs = (int32_t)(ps.rows.size() / 2);
+    TRA_HIP(dev_alloc(&m->pair_rows, ps.rows.size()));
+    TRA_HIP(dev_alloc(&m->pair_ptr, ps.ptr.size()));
+    TRA_HIP(dev_alloc(&m->u_col, ps.col.size()));
+    TRA_HIP(dev_alloc(&m->u_em, ps.em.size()));
+    TRA_HIP(dev_alloc(&m->pair_order, ps.order.size()));
+    TRA_HIP(hipMemcpy(m->pair_rows, ps.rows.data(), ps.rows.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+    TRA_HIP(hipMemcpy(m->pair_ptr, ps.ptr.data(), ps.ptr.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+    if (!ps.col.empty()) {
+        TRA_HIP(hipMemcpy(m->u_col, ps.col.data(), ps.col.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+        TRA_HIP(hipMemcpy(m->u_em, ps.em.data(), ps.em.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+    }
+    TRA_HIP(hipMemcpy(m->pair_order, ps.order.data(), ps.order.size() * sizeof(int32_t), hipMemcpyHostToDevice));
 
     {
         tra_mask_info &in = m->info;
@@ -210,6 +323,8 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
         in.min_row_blocks = *std::min_element(h_blocks.begin(), h_blocks.end());
         in.max_row_blocks = *std::max_element(h_blocks.begin(), h_blocks.end());
         in.bitmap_words = words;
+        in.work_items = m->npairs;
+        in.tile_loads = (int64_t)ps.col.size();
         in.kind = kind;
         in.granularity = p->granularity;
     }
@@ -348,8 +463,14 @@ tra_status tra_sparse_attn_fwd(const tra_tensor *Q, const tra_tensor *K, const t
     a.mask.emask_idx = mask->emask_idx;
     a.mask.emask = mask->emask;
     a.mask.order = mask->order;
+    a.mask.pair_rows = mask->pair_rows;
+    a.mask.pair_ptr = mask->pair_ptr;
+    a.mask.u_col = mask->u_col;
+    a.mask.u_em = mask->u_em;
+    a.mask.pair_order = mask->pair_order;
     a.mask.queue = mask->queue;
     a.mask.nqb = (int32_t)mask->info.nqb;
+    a.mask.npairs = mask->npairs;
     hipStream_t st = (hipStream_t)hip_stream;
     e = Q->dtype == TRA_BF16 ? tra::launch_attn_bf16(a, st) : tra::launch_attn_f32(a, st);
     return hip_status(e);

@@ -9,6 +9,14 @@
 namespace tra {
 
 constexpr int kBlock = 128;  // mask block edge (Radial Attention section 6)
+// Work distribution: query blocks are grouped in chunks of kChunk consecutive
+// blocks; chunk g of the (batch * head)-major chunk list belongs to the queue
+// of XCD g % kQueues.  The queue buffer holds kQueues counters and one
+// finished-workgroup counter.
+constexpr int kChunk = 64;      // query blocks per chunk (one per workgroup slot)
+constexpr int kPairChunk = 32;  // query-block pairs per chunk
+constexpr int kQueues = 8;
+constexpr int kQueueWords = 16;
 
 // Mask family as seen by device code.
 struct MaskDesc {
@@ -21,15 +29,31 @@ struct MaskDesc {
 // Block class written by the classifier.
 enum : uint8_t { kEmpty = 0, kFull = 1, kPartial = 2 };
 
+// Emask index of a union-schedule entry for a query block that does not keep
+// the entry's key block.
+constexpr int32_t kAbsent = -2;
+
 // Device view of a compiled mask, passed to the attention kernels by value.
+//
+// Besides the per-query-block CSR, the builder pairs query blocks whose kept
+// key blocks largely coincide (greedy, by Jaccard overlap) and stores, per
+// pair, the sorted union of their key blocks with one emask index per member
+// (-1 full, >= 0 bitmask, kAbsent not kept).  A kernel that serves both
+// members of a pair from one K/V tile halves the tile traffic.
 struct MaskDev {
     const int32_t *row_ptr;    // [nqb + 1]
     const int32_t *col_idx;    // [nnz]
     const int32_t *emask_idx;  // [nnz], -1 = full block
     const uint32_t *emask;     // [npartial][128][4]
-    const int32_t *order;      // [nqb] query blocks, heaviest first
-    uint32_t *queue;           // [2] work-queue counter, finished-group counter
+    const int32_t *order;      // [nqb] chunk-wise heaviest-first query blocks
+    const int32_t *pair_rows;  // [npairs][2] query blocks (second = -1: unpaired)
+    const int32_t *pair_ptr;   // [npairs + 1] offsets into the union schedule
+    const int32_t *u_col;      // [nunion] key block
+    const int32_t *u_em;       // [nunion][2] emask index per member
+    const int32_t *pair_order; // [npairs] chunk-wise heaviest-first pairs
+    uint32_t *queue;           // [kQueueWords] XCD queue counters, finished-group counter
     int32_t nqb;
+    int32_t npairs;
 };
 
 }  // namespace tra
@@ -45,6 +69,12 @@ struct tra_mask {
     int32_t *emask_idx;
     uint32_t *emask;
     int32_t *order;
+    int32_t *pair_rows;
+    int32_t *pair_ptr;
+    int32_t *u_col;
+    int32_t *u_em;
+    int32_t *pair_order;
+    int32_t npairs;
     uint32_t *queue;
 };
 

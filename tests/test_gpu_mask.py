@@ -59,12 +59,15 @@ def check_mask(spec: oracle.MaskSpec, counts=None):
                                               err_msg=f"block ({r}, {col_idx[e]})")
                 k += 1
     assert k == got["emask"].shape[0]
-    # heaviest-first order: a permutation, non-increasing kept-block counts, ties by index
+    # chunk-wise heaviest-first order: each chunk of 64 consecutive query
+    # blocks is permuted in place, by non-increasing kept-block count, ties by index
     per_row = np.diff(row_ptr)
     order = got["order"]
-    np.testing.assert_array_equal(np.sort(order), np.arange(spec.nb))
-    keyed = [(-per_row[x], x) for x in order]
-    assert keyed == sorted(keyed)
+    for c0 in range(0, spec.nb, 64):
+        part = order[c0:c0 + 64]
+        np.testing.assert_array_equal(np.sort(part), np.arange(c0, min(spec.nb, c0 + 64)))
+        keyed = [(-per_row[x], x) for x in part]
+        assert keyed == sorted(keyed)
     info = m.info
     assert info["n"] == spec.n and info["nqb"] == spec.nb and info["nkb"] == spec.nb
     assert info["kept_blocks"] == int((cls > 0).sum())
