@@ -120,7 +120,7 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=30.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 2 GiB device copy (counter calibration)")
     args = ap.parse_args()
