@@ -10,7 +10,10 @@ Definitions followed (pages on the method; see ``oracle.h`` for detail):
   * Radial Attention, section 3, eq. 4 -- the radial mask over frames/positions
   * Token Radius Attention, radius design section -- (r_t, r_s) neighbourhood
   * Vera 1.1 temporal module, sections 2.1-2.2 -- frame sliding-window causal
-  * Radial Attention, section 6 -- 128 x 128 block granularity
+  * Radial Attention, section 6 -- 128 x 128 block granularity (any-element
+    dilation, or eq. 4 on block indices as a second reading)
+  * Radial Attention, section 4 -- the "sink" of the complexity count, as
+    key frames every query keeps (sink_frames)
 
 The C part (``oracle.c``) does the arithmetic; this module only marshals numpy
 arrays through ctypes.
@@ -27,11 +30,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 DENSE, RADIAL, RADIUS3D, SWA = 0, 1, 2, 3
-ELEMENT, BLOCK_ANY = 0, 1
+ELEMENT, BLOCK_ANY, BLOCK_EQ4 = 0, 1, 2
 F32, BF16 = 0, 1
 
 KIND_BY_NAME = {"dense": DENSE, "radial": RADIAL, "radius3d": RADIUS3D, "swa": SWA}
-GRAN_BY_NAME = {"element": ELEMENT, "block_any": BLOCK_ANY}
+GRAN_BY_NAME = {"element": ELEMENT, "block_any": BLOCK_ANY, "block_eq4": BLOCK_EQ4}
 
 
 def build(force: bool = True) -> str:
@@ -50,7 +53,8 @@ class _Mask(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("granularity", ctypes.c_int32),
                 ("f", ctypes.c_int64), ("s", ctypes.c_int64), ("block", ctypes.c_int64),
                 ("grid_h", ctypes.c_int64), ("grid_w", ctypes.c_int64),
-                ("r_t", ctypes.c_int64), ("r_s", ctypes.c_int64), ("window", ctypes.c_int64)]
+                ("r_t", ctypes.c_int64), ("r_s", ctypes.c_int64), ("window", ctypes.c_int64),
+                ("sink_frames", ctypes.c_int64)]
 
 
 _lib = None
@@ -66,6 +70,9 @@ def _load():
         lib.orc_keep.argtypes = [P(_Mask), ctypes.c_int64, ctypes.c_int64]
         lib.orc_keep.restype = ctypes.c_int
         lib.orc_elem_matrix.argtypes = [P(_Mask), ctypes.c_void_p]
+        lib.orc_keep_block_eq4.argtypes = [P(_Mask), ctypes.c_int64, ctypes.c_int64]
+        lib.orc_keep_block_eq4.restype = ctypes.c_int
+        lib.orc_block_keep.argtypes = [P(_Mask), ctypes.c_void_p, ctypes.c_int]
         lib.orc_block_counts.argtypes = [P(_Mask), ctypes.c_void_p, ctypes.c_int]
         lib.orc_block_counts_rows.argtypes = [P(_Mask), ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                               ctypes.c_int]
@@ -92,11 +99,15 @@ class MaskSpec:
     """A mask family with its parameters (kind and granularity by name)."""
 
     def __init__(self, kind: str, f: int, s: int, granularity: str = "element", block: int = 128,
-                 grid_h: int = 0, grid_w: int = 0, r_t: int = 0, r_s: int = 0, window: int = 0):
+                 grid_h: int = 0, grid_w: int = 0, r_t: int = 0, r_s: int = 0, window: int = 0,
+                 sink_frames: int = 0):
         self.kind, self.granularity = kind, granularity
         self.f, self.s, self.block = int(f), int(s), int(block)
         self.grid_h, self.grid_w = int(grid_h), int(grid_w)
         self.r_t, self.r_s, self.window = int(r_t), int(r_s), int(window)
+        self.sink_frames = int(sink_frames)
+        if granularity == "block_eq4":
+            assert kind == "radial" and self.s % self.block == 0, "block_eq4 needs radial, s % block == 0"
 
     @property
     def n(self) -> int:
@@ -108,7 +119,8 @@ class MaskSpec:
 
     def _c(self) -> _Mask:
         return _Mask(KIND_BY_NAME[self.kind], GRAN_BY_NAME[self.granularity], self.f, self.s,
-                     self.block, self.grid_h, self.grid_w, self.r_t, self.r_s, self.window)
+                     self.block, self.grid_h, self.grid_w, self.r_t, self.r_s, self.window,
+                     self.sink_frames)
 
 
 def keep(spec: MaskSpec, q: int, t: int) -> bool:
@@ -121,6 +133,19 @@ def element_matrix(spec: MaskSpec) -> np.ndarray:
     out = np.zeros((spec.n, spec.n), dtype=np.uint8)
     m = spec._c()
     _load().orc_elem_matrix(ctypes.byref(m), out.ctypes.data)
+    return out
+
+
+def keep_block_eq4(spec: MaskSpec, bq: int, bk: int) -> bool:
+    m = spec._c()
+    return bool(_load().orc_keep_block_eq4(ctypes.byref(m), bq, bk))
+
+
+def block_keep(spec: MaskSpec, threads: int | None = None) -> np.ndarray:
+    """nb x nb uint8 kept-block matrix at the spec's granularity."""
+    out = np.zeros((spec.nb, spec.nb), dtype=np.uint8)
+    m = spec._c()
+    _load().orc_block_keep(ctypes.byref(m), out.ctypes.data, threads or default_threads())
     return out
 
 

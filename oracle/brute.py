@@ -14,7 +14,10 @@ agreement pins the C oracle's integer rewrites:
     query on the (T, H, W) grid, like the offset loops of the Token Radius
     Attention demo, and drops offsets that leave the grid (no padding);
   * the sliding window lists, for each query frame i, the key frames
-    max(0, i - W + 1) .. i of the Vera 1.1 temporal module section 2.2.
+    max(0, i - W + 1) .. i of the Vera 1.1 temporal module section 2.2;
+  * sink frames (the "sink" of Radial Attention section 4's count) set whole
+    key-frame columns of an existing matrix;
+  * the block-index reading of section 6 reuses ``radial`` on the block grid.
 """
 from __future__ import annotations
 
@@ -80,3 +83,18 @@ def dilate_any(elem: np.ndarray, block: int) -> np.ndarray:
                 keep[a, b] = 1
                 out[a * block:(a + 1) * block, b * block:(b + 1) * block] = 1
     return out, keep
+
+
+def with_sink(elem: np.ndarray, s: int, sink_frames: int) -> np.ndarray:
+    """Every query also keeps every key of frames 0 .. sink_frames - 1."""
+    out = elem.copy()
+    out[:, :min(elem.shape[1], sink_frames * s)] = 1
+    return out
+
+
+def radial_blocks(f: int, s: int, block: int, sink_frames: int = 0) -> np.ndarray:
+    """Kept-block matrix of eq. 4 applied to block indices: the block grid is
+    a video of f frames with s / block blocks per frame."""
+    assert s % block == 0
+    sb = s // block
+    return with_sink(radial(f, sb), sb, sink_frames)

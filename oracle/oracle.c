@@ -75,6 +75,10 @@ static int keep_swa(const orc_mask *m, int64_t q, int64_t t)
 
 int orc_keep(const orc_mask *m, int64_t q, int64_t t)
 {
+    /* Sink: the keys of the first sink_frames frames are kept by every query
+     * (the frame length is s for every family; RADIUS3D has s = H * W). */
+    if (t / m->s < m->sink_frames)
+        return 1;
     switch (m->kind) {
     case ORC_DENSE:
         return 1;
@@ -87,6 +91,34 @@ int orc_keep(const orc_mask *m, int64_t q, int64_t t)
     default:
         return 0;
     }
+}
+
+/* Second block reading of Radial Attention section 6: the 128 x 128 blocks
+ * themselves form a video of f frames with s / block blocks per frame, and
+ * eq. 4 decides block (bq, bk) as it decides a token pair. */
+int orc_keep_block_eq4(const orc_mask *m, int64_t bq, int64_t bk)
+{
+    int64_t sb = m->s / m->block;
+    if (bk / sb < m->sink_frames)
+        return 1;
+    return keep_radial(sb, bq, bk);
+}
+
+void orc_block_keep(const orc_mask *m, uint8_t *out, int threads)
+{
+    int64_t n = m->f * m->s;
+    int64_t nb = (n + m->block - 1) / m->block;
+    if (m->granularity == ORC_BLOCK_EQ4) {
+        for (int64_t bq = 0; bq < nb; bq++)
+            for (int64_t bk = 0; bk < nb; bk++)
+                out[bq * nb + bk] = (uint8_t)orc_keep_block_eq4(m, bq, bk);
+        return;
+    }
+    int64_t *cnt = (int64_t *)malloc((size_t)(nb * nb) * sizeof(int64_t));
+    orc_block_counts(m, cnt, threads);
+    for (int64_t i = 0; i < nb * nb; i++)
+        out[i] = cnt[i] > 0;
+    free(cnt);
 }
 
 void orc_elem_matrix(const orc_mask *m, uint8_t *out)
@@ -253,6 +285,8 @@ typedef struct {
 
 static int key_kept(const attn_job *j, int64_t q, int64_t t)
 {
+    if (j->mask->granularity == ORC_BLOCK_EQ4)
+        return orc_keep_block_eq4(j->mask, q / j->mask->block, t / j->mask->block);
     if (j->mask->granularity == ORC_BLOCK_ANY) {
         int64_t nb = (j->n + j->mask->block - 1) / j->mask->block;
         return j->block_keep[(q / j->mask->block) * nb + t / j->mask->block] != 0;

@@ -20,7 +20,13 @@
  *   - Vera 1.1 temporal module, section 2.1/2.2: frame-level causal sliding
  *     window, query frame i sees key frames [max(0, i - W + 1), i].
  *   - Radial Attention, section 6: sparsity is applied on 128 x 128 blocks; a
- *     block-granularity mask keeps a whole block iff any element is kept.
+ *     block-granularity mask keeps a whole block iff any element is kept
+ *     (ORC_BLOCK_ANY), or, as a second reading, iff eq. 4 holds for the block
+ *     indices with block frames of s / block blocks (ORC_BLOCK_EQ4, radial
+ *     only, s a multiple of the block edge).
+ *   - Radial Attention, section 4 (complexity): the central-band term counts
+ *     a "sink" beside the band.  sink_frames > 0 adds it in its plainest
+ *     form: every query keeps every key of the first sink_frames frames.
  *
  * All mask arithmetic is integer.  Attention is fp64 over the exact input
  * values (bf16 or fp32, widened exactly).
@@ -34,21 +40,32 @@ extern "C" {
 #endif
 
 enum { ORC_DENSE = 0, ORC_RADIAL = 1, ORC_RADIUS3D = 2, ORC_SWA = 3 };
-enum { ORC_ELEMENT = 0, ORC_BLOCK_ANY = 1 };
+enum { ORC_ELEMENT = 0, ORC_BLOCK_ANY = 1, ORC_BLOCK_EQ4 = 2 };
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 
 typedef struct {
     int32_t kind;         /* ORC_* family                                    */
-    int32_t granularity;  /* ORC_ELEMENT or ORC_BLOCK_ANY                    */
+    int32_t granularity;  /* ORC_ELEMENT, ORC_BLOCK_ANY or ORC_BLOCK_EQ4     */
     int64_t f, s;         /* frames, tokens per frame; n = f * s             */
     int64_t block;        /* block edge for block granularity / counting     */
     int64_t grid_h, grid_w; /* RADIUS3D: s == grid_h * grid_w                */
     int64_t r_t, r_s;     /* RADIUS3D radii                                  */
     int64_t window;       /* SWA: frames seen, the current one included      */
+    int64_t sink_frames;  /* keys of frames < sink_frames kept for all rows  */
 } orc_mask;
 
-/* Element predicate of the family (granularity ignored): 1 = kept (M = 0). */
+/* Element predicate of the family (granularity ignored): 1 = kept (M = 0).
+ * Includes the sink frames. */
 int orc_keep(const orc_mask *m, int64_t q, int64_t t);
+
+/* ORC_BLOCK_EQ4 block predicate: eq. 4 on (query block bq, key block bk)
+ * with s / block blocks per frame, or bk inside the sink frames. */
+int orc_keep_block_eq4(const orc_mask *m, int64_t bq, int64_t bk);
+
+/* nb x nb kept-block matrix of the mask at its granularity (row = query
+ * block): non-empty blocks for ORC_ELEMENT and ORC_BLOCK_ANY, the block
+ * predicate for ORC_BLOCK_EQ4. */
+void orc_block_keep(const orc_mask *m, uint8_t *out, int threads);
 
 /* Dense n x n element matrix of the family's predicate (row = query). */
 void orc_elem_matrix(const orc_mask *m, uint8_t *out);
@@ -77,7 +94,8 @@ void orc_block_bits128(const orc_mask *m, int64_t qb, int64_t kb, uint32_t *out)
  *   mask    : the family; with ORC_BLOCK_ANY a key is kept iff its block
  *             is kept in block_keep (nb x nb bytes, row = query block), which
  *             the caller fills from orc_block_counts (> 0).  block_keep is
- *             ignored for ORC_ELEMENT.
+ *             ignored for ORC_ELEMENT and ORC_BLOCK_EQ4 (the latter tests
+ *             orc_keep_block_eq4 for every key).
  *   scale   : multiplies Q K^T (1/sqrt(d) for eq. 1 and eq. 2)
  *   rows    : nrows triples (b, h, query index)
  *   o_out   : nrows x d; lse_out: nrows (natural log of the softmax

@@ -9,7 +9,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
-from oracle import MaskSpec
+from oracle import MaskSpec, brute
 
 
 def _inputs(B, H, n, d, dtype, seed, scale=1.0):
@@ -38,6 +38,17 @@ def _dilated(spec):
     return np.kron(keep.astype(np.uint8), np.ones((b, b), np.uint8))[:spec.n, :spec.n]
 
 
+def _keep_matrix(spec):
+    """Element view of the mask built without the oracle's mask code where
+    possible (brute force for the block-index reading)."""
+    if spec.granularity == "element":
+        return oracle.element_matrix(spec)
+    if spec.granularity == "block_eq4":
+        keep = brute.radial_blocks(spec.f, spec.s, spec.block, spec.sink_frames)
+        return np.kron(keep, np.ones((spec.block, spec.block), np.uint8))
+    return _dilated(spec)
+
+
 SPECS = [
     MaskSpec("radial", 6, 16),
     MaskSpec("radial", 24, 3),                      # reaches eq. 4 case (b)
@@ -46,17 +57,21 @@ SPECS = [
     MaskSpec("dense", 3, 20),
     MaskSpec("radial", 16, 16, granularity="block_any"),
     MaskSpec("radial", 5, 80, granularity="block_any"),   # n = 400: ragged last block
+    MaskSpec("radial", 6, 16, sink_frames=1),
+    MaskSpec("swa", 6, 10, window=2, sink_frames=1),
+    MaskSpec("radial", 12, 16, granularity="block_eq4", block=8),
+    MaskSpec("radial", 9, 16, granularity="block_eq4", block=4, sink_frames=1),
 ]
 
 
-@pytest.mark.parametrize("spec", SPECS, ids=lambda s: f"{s.kind}-{s.granularity}-{s.f}x{s.s}")
+@pytest.mark.parametrize("spec", SPECS, ids=lambda s: f"{s.kind}-{s.granularity}-{s.f}x{s.s}-sink{s.sink_frames}")
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_matches_sdpa_float64(spec, dtype):
     """eq. 2 with M from the family equals torch SDPA with the boolean mask."""
     B, H, d = 2, 2, 16
     q, k, v = _inputs(B, H, spec.n, d, dtype, seed=11)
     o, lse = oracle.attention_rows(_np(q), _np(k), _np(v), spec, threads=4)
-    keep = oracle.element_matrix(spec) if spec.granularity == "element" else _dilated(spec)
+    keep = _keep_matrix(spec)
     ref = _sdpa64(q, k, v, keep).reshape(-1, d).numpy()
     np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
     # LSE: log of the softmax denominator of the kept scaled scores.

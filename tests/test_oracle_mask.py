@@ -280,3 +280,65 @@ def test_block_counts_rows_subset():
     full = oracle.block_counts(spec)
     rows = np.array([3, 0, 2], dtype=np.int64)
     np.testing.assert_array_equal(oracle.block_counts_rows(spec, rows, threads=2), full[rows])
+
+
+# ---------------------------------------------------------------- sink frames
+
+@pytest.mark.parametrize("spec,base", [
+    (MaskSpec("radial", 9, 4, sink_frames=1), lambda: brute.radial(9, 4)),
+    (MaskSpec("radial", 33, 3, sink_frames=2), lambda: brute.radial(33, 3)),
+    (MaskSpec("radius3d", 4, 12, grid_h=3, grid_w=4, r_t=1, r_s=1, sink_frames=1),
+     lambda: brute.radius3d(4, 3, 4, 1, 1)),
+    (MaskSpec("swa", 7, 5, window=2, sink_frames=1), lambda: brute.swa_causal(7, 5, 2)),
+], ids=["radial", "radial-f33-sink2", "radius", "swa"])
+def test_sink_matches_bruteforce(spec, base):
+    """Sink reading of Radial Attention section 4's count: the family's mask
+    plus every key of the first sink_frames frames, for every query."""
+    np.testing.assert_array_equal(oracle.element_matrix(spec), brute.with_sink(base(), spec.s, spec.sink_frames))
+
+
+def test_sink_degenerate():
+    """sink_frames = 0 changes nothing; sink_frames >= f keeps everything."""
+    np.testing.assert_array_equal(oracle.element_matrix(radial(10, 6, sink_frames=0)), brute.radial(10, 6))
+    assert oracle.element_matrix(radial(10, 6, sink_frames=10)).all()
+    assert oracle.element_matrix(MaskSpec("swa", 5, 4, window=1, sink_frames=7)).all()
+
+
+@pytest.mark.parametrize("f,s", [(8, 16), (20, 5), (3, 9)])
+def test_sink_central_band_count(f, s):
+    """Section 4 counts "central band + sink" as 4 s^2 f.  With one sink frame
+    the frame pairs with |i - j| <= 1 or j = 0 are all kept: the band has
+    3f - 2 frame pairs, the sink adds the f - 2 pairs (i >= 2, j = 0) it does
+    not already hold, so they hold exactly s^2 (4f - 4) <= 4 s^2 f entries."""
+    m = oracle.element_matrix(radial(f, s, sink_frames=1)).astype(bool)
+    fi = np.arange(f * s) // s
+    sel = (np.abs(fi[:, None] - fi[None, :]) <= 1) | (fi[None, :] == 0)
+    assert m[sel].all()
+    assert int(sel.sum()) == s * s * (4 * f - 4) <= 4 * s * s * f
+
+
+# ---------------------------------------------------------------- eq. 4 on block indices
+
+@pytest.mark.parametrize("f,s,block,sink", [(9, 8, 4, 0), (33, 12, 4, 0), (17, 6, 2, 1), (64, 4, 4, 0),
+                                            (5, 16, 8, 2)])
+def test_block_eq4_matches_bruteforce(f, s, block, sink):
+    """Second block reading of section 6: eq. 4 on (query block, key block)
+    with s / block blocks per frame (brute force on the block grid)."""
+    spec = MaskSpec("radial", f, s, granularity="block_eq4", block=block, sink_frames=sink)
+    np.testing.assert_array_equal(oracle.block_keep(spec), brute.radial_blocks(f, s, block, sink))
+
+
+def test_block_eq4_headline_count():
+    """n = 131072 (f = 128, s = 1024, 128 x 128 blocks, 8 blocks per frame):
+    the frame-pair closed form at s = 8 gives 111,552 kept blocks of
+    1,048,576 (89.4% sparse)."""
+    expect = sum(_pair_count_closed_form(8, abs(i - j)) for i in range(128) for j in range(128))
+    assert expect == 111552
+    spec = MaskSpec("radial", 128, 1024, granularity="block_eq4")
+    assert int(oracle.block_keep(spec).sum()) == expect
+
+
+def test_block_keep_matches_counts():
+    """block_keep at element / block_any granularity = non-empty blocks."""
+    for spec in (MaskSpec("radial", 12, 40), MaskSpec("radial", 7, 100, granularity="block_any")):
+        np.testing.assert_array_equal(oracle.block_keep(spec), oracle.block_counts(spec) > 0)
