@@ -68,7 +68,7 @@ def cpu_baseline(w, q, k, v, mask_info, target_s: float):
     from oracle import MaskSpec
 
     spec = MaskSpec(w.kind, w.f, w.s, granularity=w.granularity, grid_h=w.grid_h, grid_w=w.grid_w,
-                    r_t=w.r_t, r_s=w.r_s, window=w.window)
+                    r_t=w.r_t, r_s=w.r_s, window=w.window, sink_frames=w.sink_frames)
     threads = oracle.default_threads()
     rng = np.random.default_rng(w.seed)
     nb = spec.nb
@@ -79,6 +79,8 @@ def cpu_baseline(w, q, k, v, mask_info, target_s: float):
         counts = oracle.block_counts_rows(spec, qblocks, threads)
         block_keep = np.zeros((nb, nb), dtype=np.uint8)
         block_keep[qblocks] = counts > 0
+    elif spec.granularity == "block_eq4":
+        block_keep = oracle.block_keep(spec)  # for counting kept keys; the oracle tests blocks itself
     sel = lambda x: np.stack([workloads.to_oracle_array(x[b, h]) for b, h in heads])[None]
     qa, ka, va = sel(q), sel(k), sel(v)
     cand = np.array([(0, hi, qb * 128 + r) for hi in range(len(heads)) for qb in qblocks
@@ -115,8 +117,8 @@ def cpu_baseline(w, q, k, v, mask_info, target_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -191,6 +193,7 @@ def main():
     extra = {
         "mask_build_ms": round(build_ms, 3),
         "launch_ms_mean": round(launch_ms, 4),
+        "launch_ms_median": round(float(np.median(ev_ms)), 4),
         "launch_ms_p10": round(float(np.percentile(ev_ms, 10)), 4),
         "launch_ms_p90": round(float(np.percentile(ev_ms, 90)), 4),
         "tflops_kept_elements": round(flops_elems / (launch_ms * 1e-3) / 1e12, 2),
@@ -218,6 +221,28 @@ def main():
                       "dense_tflops": round(dflops / (dense_ms * 1e-3) / 1e12, 2),
                       "speedup_vs_dense": round(dense_ms / launch_ms, 3)})
         dmask.free()
+
+    if not args.no_dense and name == workloads.HEADLINE:
+        # second block reading on the same inputs: eq. 4 on block indices
+        w2 = workloads.WORKLOADS["radial_f128_s1024_block_eq4"]
+        m2 = tra.build_mask(w2.f, w2.s, w2.kind, **w2.mask_kwargs())
+        tra.sparse_attn_fwd(q, k, v, m2, out=out, lse=lse, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            tra.sparse_attn_fwd(q, k, v, m2, out=out, lse=lse, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eq4_ms = e0.elapsed_time(e1) / reps
+        eflops = 4.0 * w.D * 128 * 128 * m2.info["kept_blocks"] * bh
+        extra.update({"block_eq4_workload": w2.name,
+                      "block_eq4_kept_blocks_per_head": m2.info["kept_blocks"],
+                      "block_eq4_ms": round(eq4_ms, 3),
+                      "block_eq4_tflops": round(eflops / (eq4_ms * 1e-3) / 1e12, 2),
+                      "block_eq4_pct_bf16_peak": round(100 * eflops / (eq4_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2)})
+        m2.free()
 
     cpu = None
     if not args.no_cpu_baseline:

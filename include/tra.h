@@ -27,11 +27,18 @@
  *                        max(0, i - window + 1) .. i.
  *   TRA_MASK_DENSE       every entry kept (eq. 1).
  *
+ * Any family may add sink frames: every query also keeps every key of the
+ * first sink_frames frames (the "sink" beside the central band in Radial
+ * Attention section 4's count; the pages give no other form of it).
+ *
  * Radial Attention section 6 applies sparsity on 128 x 128 blocks; the mask
  * is compiled once into a block bitmap, a per-query-block CSR list of kept
  * key blocks and 128 x 128 element bitmasks for the kept blocks that are only
  * partly kept.  TRA_GRAN_BLOCK_ANY keeps a whole block iff any element in it
- * is kept.
+ * is kept.  TRA_GRAN_BLOCK_EQ4 (radial only) reads the block sparsity as eq. 4
+ * applied to the block indices, with s / 128 blocks per frame: a block is
+ * kept or dropped whole by the same rule that keeps a token pair (sink frames
+ * keep whole block columns).
  *
  * Conventions for every call:
  *   - Return TRA_OK (0) or a negative tra_status.  Argument, shape, dtype and
@@ -70,7 +77,8 @@ typedef enum {
 
 typedef enum {
     TRA_GRAN_ELEMENT = 0,   /* exact element mask; partial blocks carry bits */
-    TRA_GRAN_BLOCK_ANY = 1  /* 128 x 128 block kept iff any element kept     */
+    TRA_GRAN_BLOCK_ANY = 1, /* 128 x 128 block kept iff any element kept     */
+    TRA_GRAN_BLOCK_EQ4 = 2  /* eq. 4 on block indices (radial, s % 128 == 0) */
 } tra_granularity;
 
 typedef enum { TRA_F32 = 0, TRA_BF16 = 1 } tra_dtype;
@@ -81,6 +89,8 @@ typedef enum { TRA_F32 = 0, TRA_BF16 = 1 } tra_dtype;
  *   grid_h/w     RADIUS3D: s == grid_h * grid_w, grid_h, grid_w >= 1
  *   r_t, r_s     RADIUS3D radii, >= 0
  *   window       SWA_CAUSAL: frames seen including the current one, >= 1
+ *   sink_frames  any family: leading key frames kept for every query, >= 0
+ *                (values above f act as f)
  *   reserved     must be 0                                                  */
 typedef struct {
     int32_t granularity;
@@ -88,7 +98,8 @@ typedef struct {
     int32_t grid_h, grid_w;
     int32_t r_t, r_s;
     int32_t window;
-    int32_t reserved[9];
+    int32_t sink_frames;
+    int32_t reserved[8];
 } tra_mask_params;
 
 typedef struct tra_mask tra_mask; /* opaque; owns its device buffers */
@@ -100,7 +111,9 @@ typedef struct {
     int64_t kept_blocks;    /* CSR entries (non-empty blocks)               */
     int64_t partial_blocks; /* kept blocks that carry an element bitmask    */
     int64_t kept_elems;     /* (q, t) pairs, q, t < n, attended per (b, h)  */
-    int64_t pred_elems;     /* pairs kept by the family's element predicate */
+    int64_t pred_elems;     /* pairs kept by the family's element predicate
+                               (with sink frames; eq. 4 on tokens also for
+                               TRA_GRAN_BLOCK_EQ4)                           */
     int64_t min_row_blocks, max_row_blocks;
     int64_t bitmap_words;   /* uint32 words per bitmap row = ceil(nkb / 32) */
     int64_t work_items;     /* bf16 kernel work items per (b, h): query blocks
@@ -133,9 +146,11 @@ typedef struct {
  * is synchronous; it is meant to run once per (f, s, kind, params)).  On
  * success *out owns device memory until tra_mask_free.  On failure *out is
  * NULL.  Errors: TRA_ERR_INVALID (null out/params, f or s < 1, unknown kind
- * or granularity, negative radius, window < 1, nonzero unused field),
- * TRA_ERR_UNSUPPORTED (block not 0/128, n >= 2^31), TRA_ERR_SHAPE (RADIUS3D
- * with s != grid_h * grid_w), TRA_ERR_OOM, TRA_ERR_HIP.
+ * or granularity, negative radius or sink_frames, window < 1, nonzero unused
+ * field, TRA_GRAN_BLOCK_EQ4 with a kind other than RADIAL),
+ * TRA_ERR_UNSUPPORTED (block not 0/128, n >= 2^31, TRA_GRAN_BLOCK_EQ4 with
+ * s not a multiple of 128), TRA_ERR_SHAPE (RADIUS3D with
+ * s != grid_h * grid_w), TRA_ERR_OOM, TRA_ERR_HIP.
  */
 tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_params *params,
                           void *hip_stream, tra_mask **out);

@@ -28,7 +28,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libtra.so")
 
 KINDS = {"dense": 0, "radial": 1, "radius3d": 2, "swa": 3}
-GRANULARITIES = {"element": 0, "block_any": 1}
+GRANULARITIES = {"element": 0, "block_any": 1, "block_eq4": 2}
 _F32, _BF16 = 0, 1
 _STATUS = {0: "TRA_OK", -1: "TRA_ERR_INVALID", -2: "TRA_ERR_UNSUPPORTED", -3: "TRA_ERR_SHAPE",
            -4: "TRA_ERR_OOM", -5: "TRA_ERR_HIP"}
@@ -46,7 +46,7 @@ class MaskParams(ctypes.Structure):
     _fields_ = [("granularity", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
                 ("r_t", ctypes.c_int32), ("r_s", ctypes.c_int32), ("window", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 9)]
+                ("sink_frames", ctypes.c_int32), ("reserved", ctypes.c_int32 * 8)]
 
 
 class MaskInfo(ctypes.Structure):
@@ -161,13 +161,15 @@ class Mask:
 
 
 def build_mask(f: int, s: int, kind: str, granularity: str = "element", grid_h: int = 0,
-               grid_w: int = 0, r_t: int = 0, r_s: int = 0, window: int = 0, stream=None) -> Mask:
+               grid_w: int = 0, r_t: int = 0, r_s: int = 0, window: int = 0, sink_frames: int = 0,
+               stream=None) -> Mask:
     """Compile a static mask for n = f * s tokens (synchronous; see tra_build_mask)."""
     lib = load_library()
     p = MaskParams()
     p.granularity = GRANULARITIES[granularity]
     p.block = 128
     p.grid_h, p.grid_w, p.r_t, p.r_s, p.window = grid_h, grid_w, r_t, r_s, window
+    p.sink_frames = sink_frames
     h = ctypes.c_void_p()
     _check(lib.tra_build_mask(int(f), int(s), KINDS[kind], ctypes.byref(p), _stream_handle(stream),
                               ctypes.byref(h)), "tra_build_mask")

@@ -12,9 +12,16 @@
 //   - Token Radius Attention: one run of 2 r_s + 1 columns per grid row
 //     within r_s and per frame within r_t, cut at the grid edge;
 //   - Vera 1.1 temporal module section 2.2: one run covering the frames
-//     max(0, i - W + 1) .. i.
+//     max(0, i - W + 1) .. i;
+//   - sink frames (the "sink" of Radial Attention section 4's count): one
+//     run over the first sink_frames frames, for every query and family.
 // The builder counts and sets bits run by run instead of testing every
 // element, so one thread handles one (query token, key block) pair.
+//
+// TRA_GRAN_BLOCK_EQ4 reads section 6's block sparsity the other way: the
+// 128 x 128 blocks form a video of f frames with s / 128 blocks per frame and
+// eq. 4 keeps or drops whole blocks; the element runs still give the
+// element-predicate counts of the statistics.
 #include "tra_internal.h"
 
 namespace tra {
@@ -22,6 +29,27 @@ namespace {
 
 __device__ inline int imin(int a, int b) { return a < b ? a : b; }
 __device__ inline int imax(int a, int b) { return a > b ? a : b; }
+
+// eq. 4 for one (query, key) index pair with s positions per frame.  Used on
+// block indices; the token form is the run walk below.
+__device__ inline bool radial_keep(int s, int q, int t)
+{
+    const int i = q / s, k = q - i * s, j = t / s, l = t - j * s;
+    const int delta = i > j ? i - j : j - i;
+    const int r = 31 - __clz(delta > 1 ? delta : 1);
+    const long long p2 = 1ll << r;
+    if (p2 <= s)
+        return (long long)((k > l ? k - l : l - k) + 1) * p2 <= s;
+    const long long stride = (p2 + s - 1) / s;
+    return delta % stride == 0 && k == l;
+}
+
+// Block predicate of TRA_GRAN_BLOCK_EQ4 (radial, s a multiple of 128).
+__device__ inline bool block_eq4_keep(const MaskDesc &m, int qb, int kb)
+{
+    const int sb = m.s / kBlock;
+    return kb / sb < m.sink_frames || radial_keep(sb, qb, kb);
+}
 
 // Calls fn(lo, hi) for every kept run of keys of query q, cut to [a, b)
 // and non-empty.  Runs never overlap.
@@ -34,6 +62,15 @@ __device__ void for_each_run(const MaskDesc &m, int q, int a, int b, Fn &&fn)
         if (lo < hi)
             fn(lo, hi);
     };
+    // Sink frames first; the family's runs then start past them.
+    if (m.sink_frames > 0) {
+        const long long sink_end = (long long)m.sink_frames * m.s;
+        const int end = sink_end < m.n ? (int)sink_end : m.n;
+        emit(0, end);
+        a = imax(a, end);
+        if (a >= b)
+            return;
+    }
     switch (m.kind) {
     case TRA_MASK_DENSE:
         emit(a, b);
@@ -114,11 +151,13 @@ __global__ __launch_bounds__(128) void k_classify(MaskDesc m, int nkb, uint8_t *
         const int rows_in = imin(kBlock, m.n - qb * kBlock);
         const int cols_in = b - a;
         uint8_t k;
-        if (total == 0)
+        if (m.granularity == TRA_GRAN_BLOCK_EQ4)
+            k = block_eq4_keep(m, qb, kb) ? kFull : kEmpty;  // n is a multiple of 128 here
+        else if (total == 0)
             k = kEmpty;
         else if (cols_in < kBlock)
             k = kPartial;  // keys past n must be masked
-        else if (m.granularity == TRA_GRAN_BLOCK_ANY || total == rows_in * cols_in)
+        else if (m.granularity != TRA_GRAN_ELEMENT || total == rows_in * cols_in)
             k = kFull;
         else
             k = kPartial;

@@ -174,11 +174,20 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
         return TRA_ERR_INVALID;
     if (kind < TRA_MASK_DENSE || kind > TRA_MASK_SWA_CAUSAL)
         return TRA_ERR_INVALID;
-    if (p->granularity != TRA_GRAN_ELEMENT && p->granularity != TRA_GRAN_BLOCK_ANY)
+    if (p->granularity != TRA_GRAN_ELEMENT && p->granularity != TRA_GRAN_BLOCK_ANY &&
+        p->granularity != TRA_GRAN_BLOCK_EQ4)
         return TRA_ERR_INVALID;
-    for (int i = 0; i < 9; ++i)
+    for (int i = 0; i < 8; ++i)
         if (p->reserved[i] != 0)
             return TRA_ERR_INVALID;
+    if (p->sink_frames < 0)
+        return TRA_ERR_INVALID;
+    if (p->granularity == TRA_GRAN_BLOCK_EQ4) {
+        if (kind != TRA_MASK_RADIAL)
+            return TRA_ERR_INVALID;
+        if (s % tra::kBlock != 0)
+            return TRA_ERR_UNSUPPORTED;
+    }
     if (p->block != 0 && p->block != tra::kBlock)
         return TRA_ERR_UNSUPPORTED;
     const bool radius = kind == TRA_MASK_RADIUS3D, swa = kind == TRA_MASK_SWA_CAUSAL;
@@ -218,6 +227,7 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
     d.r_t = p->r_t;
     d.r_s = p->r_s;
     d.window = p->window;
+    d.sink_frames = (int32_t)std::min<int64_t>(p->sink_frames, f);
 
     hipStream_t st = (hipStream_t)hip_stream;
     tra_status st_ = TRA_OK;

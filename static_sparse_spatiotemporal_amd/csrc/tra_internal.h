@@ -24,6 +24,7 @@ struct MaskDesc {
     int32_t granularity;
     int32_t n, f, s;
     int32_t grid_h, grid_w, r_t, r_s, window;
+    int32_t sink_frames;
 };
 
 // Block class written by the classifier.

@@ -26,6 +26,8 @@ def block_classes(spec: oracle.MaskSpec, counts: np.ndarray | None = None):
     cls = np.zeros((nb, nb), dtype=np.uint8)
     kept = counts > 0
     ragged_cols = np.broadcast_to(cols_in[None, :] < BLOCK, cls.shape)
+    if spec.granularity == "block_eq4":
+        kept = oracle.block_keep(spec) > 0  # whole blocks; n is a multiple of 128
     if spec.granularity == "element":
         partial = kept & (ragged_cols | (counts != area))
     else:
@@ -79,7 +81,7 @@ def partial_bits(spec: oracle.MaskSpec, qb: int, kb: int) -> np.ndarray:
 def kept_keys_per_row(spec: oracle.MaskSpec, cls: np.ndarray, counts_elem_rows=None) -> np.ndarray:
     """Keys attended by every query row at block granularity (kept blocks,
     cut at n)."""
-    assert spec.granularity == "block_any"
+    assert spec.granularity in ("block_any", "block_eq4")
     nb, n = spec.nb, spec.n
     cols_in = np.minimum(BLOCK, n - np.arange(nb) * BLOCK)
     per_block_row = (cls > 0).astype(np.int64) @ cols_in
@@ -90,9 +92,10 @@ _COUNT_CACHE: dict = {}
 
 
 def cached_block_counts(spec: oracle.MaskSpec) -> np.ndarray:
-    """oracle.block_counts memoised per mask (the largest masks take seconds)."""
-    key = (spec.kind, spec.granularity, spec.f, spec.s, spec.block, spec.grid_h, spec.grid_w,
-           spec.r_t, spec.r_s, spec.window)
+    """oracle.block_counts memoised per element predicate (the largest masks
+    take seconds); the counts do not depend on the granularity."""
+    key = (spec.kind, spec.f, spec.s, spec.block, spec.grid_h, spec.grid_w,
+           spec.r_t, spec.r_s, spec.window, spec.sink_frames)
     if key not in _COUNT_CACHE:
         _COUNT_CACHE[key] = oracle.block_counts(spec)
     return _COUNT_CACHE[key]

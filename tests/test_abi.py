@@ -61,6 +61,10 @@ def _params(**kw):
     (8, 12, 2, {"grid_h": 3, "grid_w": 4, "r_t": -1}, -1),
     (8, 12, 2, {"grid_h": 0, "grid_w": 4}, -1),
     (1 << 20, 1 << 12, 1, {}, -2),          # n >= 2^31
+    (8, 8, 1, {"sink_frames": -1}, -1),     # negative sink
+    (8, 256, 3, {"granularity": 2, "window": 2}, -1),  # eq. 4 on blocks is radial only
+    (8, 200, 1, {"granularity": 2}, -2),    # ... and needs s % 128 == 0
+    (8, 8, 1, {"granularity": 3}, -1),      # unknown granularity
 ])
 def test_build_mask_rejects_on_host(lib, f, s, kind, kw, expect):
     out = ctypes.c_void_p(123)

@@ -30,7 +30,8 @@ def tra():
 
 def spec_of(w: workloads.Workload) -> oracle.MaskSpec:
     return oracle.MaskSpec(w.kind, w.f, w.s, granularity=w.granularity, grid_h=w.grid_h,
-                           grid_w=w.grid_w, r_t=w.r_t, r_s=w.r_s, window=w.window)
+                           grid_w=w.grid_w, r_t=w.r_t, r_s=w.r_s, window=w.window,
+                           sink_frames=w.sink_frames)
 
 
 def build(tra, w):
@@ -73,7 +74,8 @@ def run_and_compare(tra, w, q, k, v, rows=None, mask=None, block_keep=None, tag=
 
 
 SMALL = ["radial_f8_s64_fp32", "radius3d_t8_h16_w16"]
-LARGE = ["swa_f64_s256_w16", "radial_f20_s1536_block", "radial_f128_s1024_block"]
+LARGE = ["swa_f64_s256_w16", "radial_f20_s1536_block", "radial_f128_s1024_block",
+         "radial_f128_s1024_block_eq4"]
 
 
 @pytest.mark.parametrize("name", SMALL)
@@ -96,7 +98,7 @@ def test_workload_sampled_parity(tra, name):
 
 
 @pytest.mark.parametrize("name", ["radius3d_t8_h16_w16", "swa_f64_s256_w16", "radial_f20_s1536_block",
-                                  "radial_f128_s1024_block"])
+                                  "radial_f128_s1024_block", "radial_f128_s1024_block_eq4"])
 def test_zero_query_probe(tra, name):
     """Q = 0: LSE of every row must be ln(#kept keys of that row) (exact in
     fp32 below 2^24 keys), O the mean of V over them (sampled rows)."""
@@ -108,7 +110,7 @@ def test_zero_query_probe(tra, name):
     out, lse = tra.sparse_attn_fwd(q, k, v, mask)
     torch.cuda.synchronize()
     print(f"[q0] {name}", flush=True)
-    if spec.granularity == "block_any":
+    if spec.granularity != "element":
         counts, cls = expected.block_classes(spec, expected.cached_block_counts(spec))
         kept = expected.kept_keys_per_row(spec, cls)
     elif spec.kind == "swa":
@@ -145,6 +147,12 @@ RAGGED = [
     ("swa", 5, 128, "element", dict(window=1), 1, 2, 64, "f32"),
     ("dense", 3, 100, "element", {}, 1, 2, 128, "bf16"),
     ("dense", 4, 128, "block_any", {}, 1, 2, 128, "bf16"),
+    ("radial", 10, 50, "element", dict(sink_frames=1), 1, 2, 128, "bf16"),
+    ("radial", 7, 100, "block_any", dict(sink_frames=2), 1, 2, 64, "f32"),
+    ("swa", 9, 37, "element", dict(window=3, sink_frames=2), 1, 2, 64, "bf16"),
+    ("radial", 12, 256, "block_eq4", {}, 1, 2, 128, "bf16"),
+    ("radial", 9, 256, "block_eq4", dict(sink_frames=1), 1, 2, 64, "bf16"),
+    ("radial", 12, 256, "block_eq4", {}, 1, 2, 64, "f32"),
 ]
 
 

@@ -16,8 +16,8 @@ def _spec_from(kind, f, s, gran="element", **kw):
 CASES = {
     # the named workloads (the headline one has its own test below)
     **{name: _spec_from(w.kind, w.f, w.s, w.granularity, grid_h=w.grid_h, grid_w=w.grid_w,
-                        r_t=w.r_t, r_s=w.r_s, window=w.window)
-       for name, w in workloads.WORKLOADS.items() if name != workloads.HEADLINE},
+                        r_t=w.r_t, r_s=w.r_s, window=w.window, sink_frames=w.sink_frames)
+       for name, w in workloads.WORKLOADS.items() if w.n < 131072},
     # eq. 4 case (b) (2^r > s) only occurs with f > s
     "radial_f256_s1": _spec_from("radial", 256, 1),
     "radial_f64_s2": _spec_from("radial", 64, 2),
@@ -35,14 +35,25 @@ CASES = {
     "dense_f3_s100": _spec_from("dense", 3, 100),
     "dense_f2_s128_block": _spec_from("dense", 2, 128, "block_any"),
     "tiny_f1_s1": _spec_from("radial", 1, 1),
+    # sink frames (every family), and eq. 4 on block indices
+    "radial_f10_s50_sink1_ragged": _spec_from("radial", 10, 50, sink_frames=1),
+    "radial_f7_s100_block_sink2": _spec_from("radial", 7, 100, "block_any", sink_frames=2),
+    "radius_t3_h10_w10_sink1": _spec_from("radius3d", 3, 100, grid_h=10, grid_w=10, r_t=0, r_s=1,
+                                          sink_frames=1),
+    "swa_f9_s37_w3_sink2": _spec_from("swa", 9, 37, window=3, sink_frames=2),
+    "radial_f6_s64_sink_all": _spec_from("radial", 6, 64, sink_frames=9),
+    "radial_f40_s256_block_eq4": _spec_from("radial", 40, 256, "block_eq4"),
+    "radial_f33_s128_block_eq4": _spec_from("radial", 33, 128, "block_eq4"),
+    "radial_f20_s384_block_eq4_sink1": _spec_from("radial", 20, 384, "block_eq4", sink_frames=1),
 }
 
 
 def check_mask(spec: oracle.MaskSpec, counts=None):
     import static_sparse_spatiotemporal_amd as tra
-    print(f"[mask] {spec.kind} f={spec.f} s={spec.s} {spec.granularity}", flush=True)
+    print(f"[mask] {spec.kind} f={spec.f} s={spec.s} {spec.granularity} sink={spec.sink_frames}", flush=True)
     m = tra.build_mask(spec.f, spec.s, spec.kind, granularity=spec.granularity, grid_h=spec.grid_h,
-                       grid_w=spec.grid_w, r_t=spec.r_t, r_s=spec.r_s, window=spec.window)
+                       grid_w=spec.grid_w, r_t=spec.r_t, r_s=spec.r_s, window=spec.window,
+                       sink_frames=spec.sink_frames)
     got = m.export()
     counts, cls = expected.block_classes(spec, counts)
     row_ptr, col_idx, eidx = expected.csr(cls)
@@ -96,3 +107,11 @@ def test_headline_mask_matches_oracle():
     _, cls = check_mask(spec, counts)
     # eq. 5-6 bound on the element-level kept count (f >= 2)
     assert counts.sum() <= 4 * w.s * w.s * w.f * int(np.floor(np.log2(w.f)))
+
+
+def test_headline_block_eq4_mask_matches_oracle():
+    """Same n = 131072 video, eq. 4 on block indices: 111,552 whole blocks."""
+    w = workloads.WORKLOADS["radial_f128_s1024_block_eq4"]
+    spec = _spec_from(w.kind, w.f, w.s, w.granularity)
+    _, cls = check_mask(spec, expected.cached_block_counts(spec))
+    assert int((cls > 0).sum()) == 111552 and not (cls == 2).any()

@@ -22,7 +22,7 @@ import torch
 class Workload:
     name: str
     kind: str            # "radial" | "radius3d" | "swa" | "dense"
-    granularity: str     # "element" | "block_any"
+    granularity: str     # "element" | "block_any" | "block_eq4"
     f: int               # frames (T for the radius grid)
     s: int               # tokens per frame
     B: int
@@ -36,6 +36,7 @@ class Workload:
     r_t: int = 0
     r_s: int = 0
     window: int = 0
+    sink_frames: int = 0
     note: str = field(default="", compare=False)
 
     @property
@@ -44,7 +45,7 @@ class Workload:
 
     def mask_kwargs(self) -> dict:
         return dict(granularity=self.granularity, grid_h=self.grid_h, grid_w=self.grid_w,
-                    r_t=self.r_t, r_s=self.r_s, window=self.window)
+                    r_t=self.r_t, r_s=self.r_s, window=self.window, sink_frames=self.sink_frames)
 
     def replace(self, **kw) -> "Workload":
         d = {k: getattr(self, k) for k in self.__dataclass_fields__}
@@ -68,6 +69,10 @@ WORKLOADS = {
     # Radial eq. 4 dilated to 128 x 128 blocks, f=128 x s=1024 (n=131072), 24 heads, d=128.
     "radial_f128_s1024_block": Workload("radial_f128_s1024_block", "radial", "block_any", 128,
                                         1024, 1, 24, 128, "bf16", 1005),
+    # Same shape and inputs, second block reading: eq. 4 on block indices
+    # (8 blocks per frame), 111,552 kept blocks of 1,048,576.
+    "radial_f128_s1024_block_eq4": Workload("radial_f128_s1024_block_eq4", "radial", "block_eq4",
+                                            128, 1024, 1, 24, 128, "bf16", 1005),
 }
 
 # The headline throughput workload (n = 131072 tokens, one GPU).
