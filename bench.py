@@ -88,10 +88,7 @@ def cpu_baseline(w, q, k, v, mask_info, target_s: float):
     cand = cand[rng.permutation(len(cand))]
 
     def kept_keys(rows):
-        if block_keep is not None:
-            cols = np.minimum(128, spec.n - np.arange(nb) * 128)
-            return np.array([(block_keep[r // 128] > 0) @ cols for r in rows[:, 2]], dtype=np.int64)
-        return np.array([sum(oracle.keep(spec, int(r), t) for t in range(spec.n)) for r in rows[:, 2]])
+        return oracle.row_counts(spec, rows[:, 2], block_keep=block_keep)
 
     # calibrate on a few rows, then size the sample to about target_s seconds
     probe = cand[:threads]

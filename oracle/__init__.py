@@ -79,6 +79,8 @@ def _load():
         lib.orc_kept_elements.argtypes = [P(_Mask), ctypes.c_int]
         lib.orc_kept_elements.restype = ctypes.c_int64
         lib.orc_block_bits128.argtypes = [P(_Mask), ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        lib.orc_row_counts.argtypes = [P(_Mask), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_void_p]
         lib.orc_attention_rows.argtypes = [
             ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -178,6 +180,22 @@ def block_bits128(spec: MaskSpec, qb: int, kb: int) -> np.ndarray:
     out = np.zeros((128, 4), dtype=np.uint32)
     m = spec._c()
     _load().orc_block_bits128(ctypes.byref(m), qb, kb, out.ctypes.data)
+    return out
+
+
+def row_counts(spec: MaskSpec, rows, block_keep: np.ndarray | None = None) -> np.ndarray:
+    """Keys attended by each listed query row (int64), by the rule
+    attention_rows uses."""
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+    out = np.zeros(rows.size, dtype=np.int64)
+    bk_ptr = None
+    if spec.granularity == "block_any":
+        if block_keep is None:
+            block_keep = block_counts(spec) > 0
+        block_keep = np.ascontiguousarray(block_keep, dtype=np.uint8)
+        bk_ptr = block_keep.ctypes.data
+    m = spec._c()
+    _load().orc_row_counts(ctypes.byref(m), bk_ptr, rows.ctypes.data, rows.size, out.ctypes.data)
     return out
 
 

@@ -344,6 +344,22 @@ static void *attn_worker(void *arg)
     return NULL;
 }
 
+void orc_row_counts(const orc_mask *m, const uint8_t *block_keep, const int64_t *rows, int64_t nrows,
+                    int64_t *out)
+{
+    attn_job j;
+    memset(&j, 0, sizeof j);
+    j.n = m->f * m->s;
+    j.mask = m;
+    j.block_keep = block_keep;
+    for (int64_t r = 0; r < nrows; r++) {
+        int64_t c = 0;
+        for (int64_t t = 0; t < j.n; t++)
+            c += key_kept(&j, rows[r], t);
+        out[r] = c;
+    }
+}
+
 void orc_attention_rows(int dtype, const void *q, const void *k, const void *v,
                         int64_t B, int64_t H, int64_t n, int64_t d,
                         const orc_mask *mask, const uint8_t *block_keep,

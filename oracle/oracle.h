@@ -88,6 +88,12 @@ int64_t orc_kept_elements(const orc_mask *m, int threads);
  * key kb*128 + w*32 + b) kept; elements beyond n read as 0. */
 void orc_block_bits128(const orc_mask *m, int64_t qb, int64_t kb, uint32_t *out);
 
+/* Number of keys each listed query row attends (same rule as
+ * orc_attention_rows: element predicate, block_keep for ORC_BLOCK_ANY, the
+ * block predicate for ORC_BLOCK_EQ4).  rows: nrows query indices. */
+void orc_row_counts(const orc_mask *m, const uint8_t *block_keep, const int64_t *rows, int64_t nrows,
+                    int64_t *out);
+
 /* fp64 masked attention for a list of rows.
  *   q, k, v : [B, H, n, d] contiguous, dtype ORC_F32 (float) or ORC_BF16
  *             (raw bfloat16 bit patterns, uint16)

@@ -342,3 +342,18 @@ def test_block_keep_matches_counts():
     """block_keep at element / block_any granularity = non-empty blocks."""
     for spec in (MaskSpec("radial", 12, 40), MaskSpec("radial", 7, 100, granularity="block_any")):
         np.testing.assert_array_equal(oracle.block_keep(spec), oracle.block_counts(spec) > 0)
+
+
+def test_row_counts_match_matrices():
+    """Per-row attended-key counts equal the row sums of the element matrix,
+    or of the brute-force block matrix expanded to tokens."""
+    for spec in (MaskSpec("radial", 9, 7), MaskSpec("swa", 6, 5, window=2, sink_frames=1)):
+        rows = np.arange(spec.n)
+        np.testing.assert_array_equal(oracle.row_counts(spec, rows), oracle.element_matrix(spec).sum(1))
+    spec = MaskSpec("radial", 10, 8, granularity="block_eq4", block=4)
+    keep = np.kron(brute.radial_blocks(10, 8, 4), np.ones((4, 4), np.uint8))
+    np.testing.assert_array_equal(oracle.row_counts(spec, np.arange(spec.n)), keep.sum(1))
+    spec = MaskSpec("radial", 5, 80, granularity="block_any")
+    bk = oracle.block_counts(spec) > 0
+    dil = np.kron(bk.astype(np.uint8), np.ones((128, 128), np.uint8))[:spec.n, :spec.n]
+    np.testing.assert_array_equal(oracle.row_counts(spec, np.arange(spec.n), block_keep=bk), dil.sum(1))
