@@ -79,6 +79,11 @@ def _load():
         lib.orc_kept_elements.argtypes = [P(_Mask), ctypes.c_int]
         lib.orc_kept_elements.restype = ctypes.c_int64
         lib.orc_block_bits128.argtypes = [P(_Mask), ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        lib.orc_attention_bwd_rows.argtypes = [
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            P(_Mask), ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.orc_row_counts.argtypes = [P(_Mask), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_void_p]
         lib.orc_attention_rows.argtypes = [
@@ -239,3 +244,53 @@ def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, spec: MaskSpec,
                                rows.shape[0], o.ctypes.data, lse.ctypes.data,
                                threads or default_threads())
     return o, lse
+
+
+def attention_bwd_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, spec: MaskSpec,
+                       q_rows: np.ndarray | None = None, k_rows: np.ndarray | None = None,
+                       scale: float | None = None, block_keep: np.ndarray | None = None,
+                       threads: int | None = None):
+    """fp64 gradients of eq. 2 (dQ for q_rows, dK and dV for k_rows).
+
+    Arrays as attention_rows plus dout (the gradient of O).  Row lists are
+    (b, h, index) triples; None = every row.  Returns (dQ [nq, d], dK [nk, d],
+    dV [nk, d]) as float64.
+    """
+    B, H, n, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape and dout.shape == q.shape and n == spec.n
+    if q.dtype == np.float32:
+        dtype = F32
+    elif q.dtype == np.uint16:
+        dtype = BF16
+    else:
+        raise TypeError("q/k/v/dout must be float32 or uint16 (bfloat16 bits)")
+    assert k.dtype == q.dtype and v.dtype == q.dtype and dout.dtype == q.dtype
+    q, k, v, dout = (np.ascontiguousarray(a) for a in (q, k, v, dout))
+
+    def all_rows():
+        bb, hh, ii = np.meshgrid(np.arange(B), np.arange(H), np.arange(n), indexing="ij")
+        return np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)
+
+    q_rows = all_rows() if q_rows is None else q_rows
+    k_rows = all_rows() if k_rows is None else k_rows
+    q_rows = np.ascontiguousarray(q_rows, dtype=np.int64).reshape(-1, 3)
+    k_rows = np.ascontiguousarray(k_rows, dtype=np.int64).reshape(-1, 3)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    bk_ptr = None
+    if spec.granularity == "block_any":
+        if block_keep is None:
+            block_keep = block_counts(spec, threads) > 0
+        block_keep = np.ascontiguousarray(block_keep, dtype=np.uint8)
+        assert block_keep.shape == (spec.nb, spec.nb)
+        bk_ptr = block_keep.ctypes.data
+    dq = np.zeros((q_rows.shape[0], d), dtype=np.float64)
+    dk = np.zeros((k_rows.shape[0], d), dtype=np.float64)
+    dv = np.zeros((k_rows.shape[0], d), dtype=np.float64)
+    m = spec._c()
+    _load().orc_attention_bwd_rows(dtype, q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                   B, H, n, d, ctypes.byref(m), bk_ptr, float(scale),
+                                   q_rows.ctypes.data, q_rows.shape[0], dq.ctypes.data,
+                                   k_rows.ctypes.data, k_rows.shape[0], dk.ctypes.data, dv.ctypes.data,
+                                   threads or default_threads())
+    return dq, dk, dv

@@ -397,3 +397,224 @@ void orc_attention_rows(int dtype, const void *q, const void *k, const void *v,
     free(jobs);
     free(tid);
 }
+
+/* ---- backward ------------------------------------------------------------ */
+
+/* Softmax row of query q (scaled scores, masked keys -> -inf) and the row's
+ * dP entries: p[t] (0 for masked keys), dp[t] = dO[q] . V[t].  Returns
+ * rowsum(p o dp). */
+static double softmax_row(const attn_job *j, const void *dout, int64_t head, int64_t q, double *qrow,
+                          double *p, double *dp)
+{
+    const int64_t n = j->n, d = j->d;
+    for (int64_t x = 0; x < d; x++)
+        qrow[x] = load_value(j->dtype, j->q, head + q * d + x);
+    double mx = -INFINITY;
+    for (int64_t t = 0; t < n; t++) {
+        if (!key_kept(j, q, t)) {
+            p[t] = -INFINITY;
+            continue;
+        }
+        double acc = 0.0;
+        for (int64_t x = 0; x < d; x++)
+            acc += qrow[x] * load_value(j->dtype, j->k, head + t * d + x);
+        p[t] = acc * j->scale;
+        if (p[t] > mx)
+            mx = p[t];
+    }
+    double denom = 0.0;
+    for (int64_t t = 0; t < n; t++) {
+        p[t] = (p[t] == -INFINITY || mx == -INFINITY) ? 0.0 : exp(p[t] - mx);
+        denom += p[t];
+    }
+    double delta = 0.0;
+    for (int64_t t = 0; t < n; t++) {
+        if (denom > 0.0)
+            p[t] /= denom;
+        dp[t] = 0.0;
+        if (p[t] == 0.0 && !key_kept(j, q, t))
+            continue;
+        double acc = 0.0;
+        for (int64_t x = 0; x < d; x++)
+            acc += load_value(j->dtype, dout, head + q * d + x) * load_value(j->dtype, j->v, head + t * d + x);
+        dp[t] = acc;
+        delta += p[t] * acc;
+    }
+    return delta;
+}
+
+typedef struct {
+    attn_job base;
+    const void *dout;
+    const int64_t *rows;
+    int64_t begin, end;
+    double *dq, *dk, *dv;
+} bwd_job;
+
+/* dQ rows: dQ[q] = scale sum_t dS[q, t] K[t]. */
+static void *bwd_q_worker(void *arg)
+{
+    bwd_job *w = (bwd_job *)arg;
+    const attn_job *j = &w->base;
+    const int64_t n = j->n, d = j->d;
+    double *p = (double *)malloc((size_t)n * sizeof(double));
+    double *dp = (double *)malloc((size_t)n * sizeof(double));
+    double *qrow = (double *)malloc((size_t)d * sizeof(double));
+    for (int64_t r = w->begin; r < w->end; r++) {
+        int64_t b = w->rows[3 * r], h = w->rows[3 * r + 1], q = w->rows[3 * r + 2];
+        int64_t head = (b * j->H + h) * n * d;
+        double delta = softmax_row(j, w->dout, head, q, qrow, p, dp);
+        double *out = w->dq + r * d;
+        for (int64_t x = 0; x < d; x++)
+            out[x] = 0.0;
+        for (int64_t t = 0; t < n; t++) {
+            double ds = p[t] * (dp[t] - delta);
+            if (ds == 0.0)
+                continue;
+            for (int64_t x = 0; x < d; x++)
+                out[x] += ds * load_value(j->dtype, j->k, head + t * d + x);
+        }
+        for (int64_t x = 0; x < d; x++)
+            out[x] *= j->scale;
+    }
+    free(p);
+    free(dp);
+    free(qrow);
+    return NULL;
+}
+
+/* dK/dV rows of the listed keys, one (b, h) at a time: every query of the
+ * head contributes dV[t] += P[q, t] dO[q] and dK[t] += scale dS[q, t] Q[q].
+ * Threads split the queries; each keeps private sums that are added at
+ * the end (in a fixed order). */
+typedef struct {
+    attn_job base;
+    const void *dout;
+    int64_t head, q0, q1;
+    const int64_t *keys;  /* key indices of this head's listed rows */
+    int64_t nkeys;
+    double *dk, *dv;      /* nkeys x d private sums */
+} bwd_kv_job;
+
+static void *bwd_kv_worker(void *arg)
+{
+    bwd_kv_job *w = (bwd_kv_job *)arg;
+    const attn_job *j = &w->base;
+    const int64_t n = j->n, d = j->d;
+    double *p = (double *)malloc((size_t)n * sizeof(double));
+    double *dp = (double *)malloc((size_t)n * sizeof(double));
+    double *qrow = (double *)malloc((size_t)d * sizeof(double));
+    for (int64_t q = w->q0; q < w->q1; q++) {
+        int any = 0;
+        for (int64_t i = 0; i < w->nkeys && !any; i++)
+            any = key_kept(j, q, w->keys[i]);
+        if (!any)
+            continue;
+        double delta = softmax_row(j, w->dout, w->head, q, qrow, p, dp);
+        for (int64_t i = 0; i < w->nkeys; i++) {
+            int64_t t = w->keys[i];
+            if (p[t] == 0.0 && dp[t] == 0.0)
+                continue;
+            double ds = p[t] * (dp[t] - delta) * j->scale;
+            for (int64_t x = 0; x < d; x++) {
+                w->dv[i * d + x] += p[t] * load_value(j->dtype, w->dout, w->head + q * d + x);
+                w->dk[i * d + x] += ds * qrow[x];
+            }
+        }
+    }
+    free(p);
+    free(dp);
+    free(qrow);
+    return NULL;
+}
+
+void orc_attention_bwd_rows(int dtype, const void *q, const void *k, const void *v, const void *dout,
+                            int64_t B, int64_t H, int64_t n, int64_t d,
+                            const orc_mask *mask, const uint8_t *block_keep, double scale,
+                            const int64_t *q_rows, int64_t nq, double *dq_out,
+                            const int64_t *k_rows, int64_t nk, double *dk_out, double *dv_out,
+                            int threads)
+{
+    (void)B;
+    if (threads < 1)
+        threads = 1;
+    attn_job base;
+    memset(&base, 0, sizeof base);
+    base.dtype = dtype;
+    base.q = q;
+    base.k = k;
+    base.v = v;
+    base.H = H;
+    base.n = n;
+    base.d = d;
+    base.mask = mask;
+    base.block_keep = block_keep;
+    base.scale = scale;
+    pthread_t *tid = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    if (nq > 0) {
+        int tq = threads > nq ? (int)nq : threads;
+        bwd_job *jobs = (bwd_job *)calloc((size_t)tq, sizeof(bwd_job));
+        for (int w = 0; w < tq; w++) {
+            jobs[w].base = base;
+            jobs[w].dout = dout;
+            jobs[w].rows = q_rows;
+            jobs[w].begin = nq * w / tq;
+            jobs[w].end = nq * (w + 1) / tq;
+            jobs[w].dq = dq_out;
+            pthread_create(&tid[w], NULL, bwd_q_worker, &jobs[w]);
+        }
+        for (int w = 0; w < tq; w++)
+            pthread_join(tid[w], NULL);
+        free(jobs);
+    }
+    /* dK/dV: group the listed rows by head */
+    for (int64_t i = 0; i < nk * d; i++) {
+        dk_out[i] = 0.0;
+        dv_out[i] = 0.0;
+    }
+    char *done = (char *)calloc((size_t)(nk > 0 ? nk : 1), 1);
+    int64_t *idx = (int64_t *)malloc((size_t)(nk > 0 ? nk : 1) * sizeof(int64_t));
+    int64_t *keys = (int64_t *)malloc((size_t)(nk > 0 ? nk : 1) * sizeof(int64_t));
+    for (int64_t r0 = 0; r0 < nk; r0++) {
+        if (done[r0])
+            continue;
+        int64_t b = k_rows[3 * r0], h = k_rows[3 * r0 + 1];
+        int64_t cnt = 0;
+        for (int64_t r = r0; r < nk; r++)
+            if (!done[r] && k_rows[3 * r] == b && k_rows[3 * r + 1] == h) {
+                done[r] = 1;
+                idx[cnt] = r;
+                keys[cnt] = k_rows[3 * r + 2];
+                cnt++;
+            }
+        bwd_kv_job *jobs = (bwd_kv_job *)calloc((size_t)threads, sizeof(bwd_kv_job));
+        for (int w = 0; w < threads; w++) {
+            jobs[w].base = base;
+            jobs[w].dout = dout;
+            jobs[w].head = (b * H + h) * n * d;
+            jobs[w].q0 = n * w / threads;
+            jobs[w].q1 = n * (w + 1) / threads;
+            jobs[w].keys = keys;
+            jobs[w].nkeys = cnt;
+            jobs[w].dk = (double *)calloc((size_t)(cnt * d), sizeof(double));
+            jobs[w].dv = (double *)calloc((size_t)(cnt * d), sizeof(double));
+            pthread_create(&tid[w], NULL, bwd_kv_worker, &jobs[w]);
+        }
+        for (int w = 0; w < threads; w++)
+            pthread_join(tid[w], NULL);
+        for (int w = 0; w < threads; w++) {
+            for (int64_t i = 0; i < cnt; i++)
+                for (int64_t x = 0; x < d; x++) {
+                    dk_out[idx[i] * d + x] += jobs[w].dk[i * d + x];
+                    dv_out[idx[i] * d + x] += jobs[w].dv[i * d + x];
+                }
+            free(jobs[w].dk);
+            free(jobs[w].dv);
+        }
+        free(jobs);
+    }
+    free(done);
+    free(idx);
+    free(keys);
+    free(tid);
+}

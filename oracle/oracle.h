@@ -114,6 +114,25 @@ void orc_attention_rows(int dtype, const void *q, const void *k, const void *v,
                         double scale, const int64_t *rows, int64_t nrows,
                         double *o_out, double *lse_out, int threads);
 
+/* fp64 gradients of eq. 2 for a list of rows (the backward pass of the
+ * masked softmax attention).  With P the softmax of the scaled masked
+ * scores, dO the gradient of the output and scale the score scale:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - rowsum(P o dP)),
+ *   dQ = scale dS K,  dK = scale dS^T Q
+ * Inputs as orc_attention_rows plus dO (same layout and dtype).
+ *   q_rows : nq triples (b, h, query) whose dQ rows are returned in dq_out
+ *            (nq x d)
+ *   k_rows : nk triples (b, h, key) whose dK and dV rows are returned in
+ *            dk_out, dv_out (nk x d)
+ * A dK/dV row needs the softmax of every query that keeps the key, so its
+ * cost is that of a full pass over the head. */
+void orc_attention_bwd_rows(int dtype, const void *q, const void *k, const void *v, const void *dout,
+                            int64_t B, int64_t H, int64_t n, int64_t d,
+                            const orc_mask *mask, const uint8_t *block_keep, double scale,
+                            const int64_t *q_rows, int64_t nq, double *dq_out,
+                            const int64_t *k_rows, int64_t nk, double *dk_out, double *dv_out,
+                            int threads);
+
 #ifdef __cplusplus
 }
 #endif
