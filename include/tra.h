@@ -120,6 +120,9 @@ typedef struct {
                                paired by key-block overlap, plus singles     */
     int64_t tile_loads;     /* K/V tiles the bf16 kernel loads per (b, h)    */
     int32_t kind, granularity;
+    int64_t bwd_work_items; /* backward dK/dV work items per (b, h): key
+                               blocks paired by query-block overlap          */
+    int64_t bwd_tile_loads; /* Q/dO tiles the dK/dV kernel loads per (b, h)  */
 } tra_mask_info;
 
 /* A [B, H, N, D] tensor view.  stride[] in elements, order B, H, N, D;
@@ -177,6 +180,30 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
 tra_status tra_sparse_attn_fwd(const tra_tensor *Q, const tra_tensor *K, const tra_tensor *V,
                                const tra_mask *mask, tra_tensor *O, float *LSE, float scale,
                                void *hip_stream);
+
+/*
+ * tra_sparse_attn_bwd -- gradients of eq. 2 (the backward pass of
+ * tra_sparse_attn_fwd with the same mask and scale).
+ *
+ * With P the forward's probabilities (recomputed from Q, K and the saved
+ * LSE), dO the gradient of O and delta = rowsum(dO o O):
+ *   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - delta),
+ *   dK = scale dS^T Q,  dQ = scale dS K.
+ * Q, K, V, O, dO, dQ, dK, dV: [B, H, N, D] bf16 views (same rules as the
+ * forward; the gradients are accumulated in fp32 and rounded to bf16).
+ * O and LSE must be the forward outputs for these Q, K, V, mask and scale.
+ * delta: device float[B * H * N] workspace owned by the caller, overwritten.
+ * The outputs must not overlap the inputs or each other.  Asynchronous;
+ * allocates nothing; the same mask must not be used by a concurrent call.
+ * Results are deterministic (no atomics).  B == 0 or H == 0 returns TRA_OK.
+ * Errors: TRA_ERR_INVALID (null tensor/mask/data/LSE/delta), TRA_ERR_SHAPE,
+ * TRA_ERR_UNSUPPORTED (a dtype other than bf16, D not 64/128, bad stride or
+ * alignment), TRA_ERR_HIP.
+ */
+tra_status tra_sparse_attn_bwd(const tra_tensor *Q, const tra_tensor *K, const tra_tensor *V,
+                               const tra_tensor *O, const tra_tensor *dO, const float *LSE,
+                               const tra_mask *mask, tra_tensor *dQ, tra_tensor *dK, tra_tensor *dV,
+                               float *delta, float scale, void *hip_stream);
 
 /* Copy the host-side summary filled at build time.  No device work. */
 tra_status tra_mask_get_info(const tra_mask *mask, tra_mask_info *out);

@@ -21,7 +21,7 @@ import os
 import numpy as np
 import torch
 
-__all__ = ["build_mask", "sparse_attn_fwd", "Mask", "TraError", "library_path", "load_library",
+__all__ = ["build_mask", "sparse_attn_fwd", "sparse_attn_bwd", "Mask", "TraError", "library_path", "load_library",
            "KINDS", "GRANULARITIES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -57,7 +57,8 @@ class MaskInfo(ctypes.Structure):
                 ("min_row_blocks", ctypes.c_int64), ("max_row_blocks", ctypes.c_int64),
                 ("bitmap_words", ctypes.c_int64), ("work_items", ctypes.c_int64),
                 ("tile_loads", ctypes.c_int64), ("kind", ctypes.c_int32),
-                ("granularity", ctypes.c_int32)]
+                ("granularity", ctypes.c_int32), ("bwd_work_items", ctypes.c_int64),
+                ("bwd_tile_loads", ctypes.c_int64)]
 
 
 class TensorDesc(ctypes.Structure):
@@ -89,6 +90,10 @@ def load_library():
     lib.tra_sparse_attn_fwd.argtypes = [P(TensorDesc), P(TensorDesc), P(TensorDesc), vp, P(TensorDesc),
                                         vp, ctypes.c_float, vp]
     lib.tra_sparse_attn_fwd.restype = ctypes.c_int
+    lib.tra_sparse_attn_bwd.argtypes = [P(TensorDesc), P(TensorDesc), P(TensorDesc), P(TensorDesc),
+                                        P(TensorDesc), vp, vp, P(TensorDesc), P(TensorDesc), P(TensorDesc),
+                                        vp, ctypes.c_float, vp]
+    lib.tra_sparse_attn_bwd.restype = ctypes.c_int
     lib.tra_mask_get_info.argtypes = [vp, P(MaskInfo)]
     lib.tra_mask_get_info.restype = ctypes.c_int
     lib.tra_mask_export.argtypes = [vp, vp, vp, vp, vp, vp, vp]
@@ -220,3 +225,28 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mas
         ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
         float(scale) if scale else 0.0, _stream_handle(stream)), "tra_sparse_attn_fwd")
     return out, lse
+
+
+def sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                    dout: torch.Tensor, mask: Mask, scale: float | None = None, grads=None,
+                    delta: torch.Tensor | None = None, stream=None):
+    """Gradients (dQ, dK, dV) of sparse_attn_fwd on the GPU (see tra_sparse_attn_bwd).
+
+    q, k, v, out, dout: [B, H, n, D] bf16 cuda tensors; lse: the forward's
+    [B, H, n] fp32 output.  `grads` = (dq, dk, dv) output tensors (default:
+    new contiguous ones); `delta` a [B, H, n] fp32 workspace (default: new).
+    """
+    if grads is None:
+        grads = tuple(torch.empty(q.shape, dtype=q.dtype, device=q.device) for _ in range(3))
+    if delta is None:
+        delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    for t in (lse, delta):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(q.shape[:3]):
+            raise ValueError("lse and delta must be contiguous float32 [B, H, n] tensors")
+    descs = [_desc(t) for t in (q, k, v, out, dout)]
+    gd = [_desc(t) for t in grads]
+    _check(load_library().tra_sparse_attn_bwd(
+        *(ctypes.byref(d) for d in descs), ctypes.c_void_p(lse.data_ptr()), mask.handle,
+        *(ctypes.byref(d) for d in gd), ctypes.c_void_p(delta.data_ptr()),
+        float(scale) if scale else 0.0, _stream_handle(stream)), "tra_sparse_attn_bwd")
+    return grads

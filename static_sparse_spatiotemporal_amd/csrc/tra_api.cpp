@@ -133,9 +133,57 @@ void free_mask_buffers(tra_mask *m)
     hipFree(m->u_em);
     hipFree(m->pair_order);
     hipFree(m->queue);
+    hipFree(m->t_pair_cols);
+    hipFree(m->t_pair_ptr);
+    hipFree(m->t_u_row);
+    hipFree(m->t_u_em);
+    hipFree(m->t_pair_order);
 }
 
 bool tensor_ok(const tra_tensor *t) { return t != nullptr && t->data != nullptr; }
+
+// Kernel arguments shared by the forward and backward entry points (O and
+// LSE may be NULL).
+void fill_attn_args(tra::AttnArgs &a, const tra_tensor *Q, const tra_tensor *K, const tra_tensor *V,
+                    const tra_tensor *O, float *LSE, const tra_mask *mask, float scale)
+{
+    a.q = Q->data;
+    a.k = K->data;
+    a.v = V->data;
+    a.o = O ? O->data : nullptr;
+    a.lse = LSE;
+    for (int i = 0; i < 3; ++i) {
+        a.sq[i] = Q->stride[i];
+        a.sk[i] = K->stride[i];
+        a.sv[i] = V->stride[i];
+        a.so[i] = O ? O->stride[i] : 0;
+    }
+    a.B = (int32_t)Q->B;
+    a.H = (int32_t)Q->H;
+    a.N = (int32_t)Q->N;
+    a.D = (int32_t)Q->D;
+    const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)Q->D);
+    a.scale_log2 = (float)(sc * 1.4426950408889634);
+    a.mask.row_ptr = mask->row_ptr;
+    a.mask.col_idx = mask->col_idx;
+    a.mask.emask_idx = mask->emask_idx;
+    a.mask.emask = mask->emask;
+    a.mask.order = mask->order;
+    a.mask.pair_rows = mask->pair_rows;
+    a.mask.pair_ptr = mask->pair_ptr;
+    a.mask.u_col = mask->u_col;
+    a.mask.u_em = mask->u_em;
+    a.mask.pair_order = mask->pair_order;
+    a.mask.queue = mask->queue;
+    a.mask.nqb = (int32_t)mask->info.nqb;
+    a.mask.npairs = mask->npairs;
+    a.mask.t_pair_cols = mask->t_pair_cols;
+    a.mask.t_pair_ptr = mask->t_pair_ptr;
+    a.mask.t_u_row = mask->t_u_row;
+    a.mask.t_u_em = mask->t_u_em;
+    a.mask.t_pair_order = mask->t_pair_order;
+    a.mask.t_npairs = mask->t_npairs;
+}
 
 }  // namespace
 
@@ -239,7 +287,7 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
         h_order(nqb);
     std::vector<long long> h_pred(nqb), h_eff(nqb);
     std::vector<int32_t> h_col, h_em;
-    PairSchedule ps;
+    PairSchedule ps, tps;
     int64_t nnz = 0, npart = 0;
 
     TRA_HIP(hipGetDevice(&m->device));
@@ -315,6 +363,37 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
     }
     TRA_HIP(hipMemcpy(m->pair_order, ps.order.data(), ps.order.size() * sizeof(int32_t), hipMemcpyHostToDevice));
 
+    // The same schedule over key blocks, from the column lists of the mask.
+    {
+        std::vector<int32_t> col_ptr(nkb + 1, 0), row_idx(nnz), em_t(nnz);
+        for (int64_t e = 0; e < nnz; ++e)
+            col_ptr[h_col[e] + 1]++;
+        for (int c = 0; c < nkb; ++c)
+            col_ptr[c + 1] += col_ptr[c];
+        std::vector<int32_t> fill(col_ptr.begin(), col_ptr.end() - 1);
+        for (int r = 0; r < nqb; ++r)  // rows in order: each column list ascends
+            for (int32_t e = h_row_ptr[r]; e < h_row_ptr[r + 1]; ++e) {
+                const int32_t at = fill[h_col[e]]++;
+                row_idx[at] = r;
+                em_t[at] = h_em[e];
+            }
+        tps = build_pairs(nkb, s, col_ptr, row_idx, em_t);
+    }
+    m->t_npairs = (int32_t)(tps.rows.size() / 2);
+    m->t_nunion = (int64_t)tps.col.size();
+    TRA_HIP(dev_alloc(&m->t_pair_cols, tps.rows.size()));
+    TRA_HIP(dev_alloc(&m->t_pair_ptr, tps.ptr.size()));
+    TRA_HIP(dev_alloc(&m->t_u_row, tps.col.size()));
+    TRA_HIP(dev_alloc(&m->t_u_em, tps.em.size()));
+    TRA_HIP(dev_alloc(&m->t_pair_order, tps.order.size()));
+    TRA_HIP(hipMemcpy(m->t_pair_cols, tps.rows.data(), tps.rows.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+    TRA_HIP(hipMemcpy(m->t_pair_ptr, tps.ptr.data(), tps.ptr.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+    if (!tps.col.empty()) {
+        TRA_HIP(hipMemcpy(m->t_u_row, tps.col.data(), tps.col.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+        TRA_HIP(hipMemcpy(m->t_u_em, tps.em.data(), tps.em.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+    }
+    TRA_HIP(hipMemcpy(m->t_pair_order, tps.order.data(), tps.order.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+
     {
         tra_mask_info &in = m->info;
         in.n = n;
@@ -337,6 +416,8 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
         in.tile_loads = (int64_t)ps.col.size();
         in.kind = kind;
         in.granularity = p->granularity;
+        in.bwd_work_items = m->t_npairs;
+        in.bwd_tile_loads = m->t_nunion;
     }
     hipFree(cls);
     hipFree(cnt);
@@ -451,39 +532,83 @@ tra_status tra_sparse_attn_fwd(const tra_tensor *Q, const tra_tensor *K, const t
         return TRA_ERR_INVALID;
 
     tra::AttnArgs a;
-    a.q = Q->data;
-    a.k = K->data;
-    a.v = V->data;
-    a.o = O->data;
-    a.lse = LSE;
-    for (int i = 0; i < 3; ++i) {
-        a.sq[i] = Q->stride[i];
-        a.sk[i] = K->stride[i];
-        a.sv[i] = V->stride[i];
-        a.so[i] = O->stride[i];
-    }
-    a.B = (int32_t)Q->B;
-    a.H = (int32_t)Q->H;
-    a.N = (int32_t)Q->N;
-    a.D = (int32_t)Q->D;
-    const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)Q->D);
-    a.scale_log2 = (float)(sc * 1.4426950408889634);
-    a.mask.row_ptr = mask->row_ptr;
-    a.mask.col_idx = mask->col_idx;
-    a.mask.emask_idx = mask->emask_idx;
-    a.mask.emask = mask->emask;
-    a.mask.order = mask->order;
-    a.mask.pair_rows = mask->pair_rows;
-    a.mask.pair_ptr = mask->pair_ptr;
-    a.mask.u_col = mask->u_col;
-    a.mask.u_em = mask->u_em;
-    a.mask.pair_order = mask->pair_order;
-    a.mask.queue = mask->queue;
-    a.mask.nqb = (int32_t)mask->info.nqb;
-    a.mask.npairs = mask->npairs;
+    fill_attn_args(a, Q, K, V, O, LSE, mask, scale);
     hipStream_t st = (hipStream_t)hip_stream;
     e = Q->dtype == TRA_BF16 ? tra::launch_attn_bf16(a, st) : tra::launch_attn_f32(a, st);
     return hip_status(e);
 }
 
-}  // extern "C"
+tra_status tra_sparse_attn_bwd(const tra_tensor *Q, const tra_tensor *K, const tra_tensor *V, const tra_tensor *O,
+                               const tra_tensor *dO, const float *LSE, const tra_mask *mask, tra_tensor *dQ,
+                               tra_tensor *dK, tra_tensor *dV, float *delta, float scale, void *hip_stream)
+{
+    const tra_tensor *ts[9] = {Q, K, V, O, dO, dQ, dK, dV, nullptr};
+    for (int i = 0; i < 8; ++i)
+        if (ts[i] == nullptr)
+            return TRA_ERR_INVALID;
+    if (mask == nullptr)
+        return TRA_ERR_INVALID;
+    const bool empty = Q->B == 0 || Q->H == 0;
+    if (!empty) {
+        for (int i = 0; i < 8; ++i)
+            if (!tensor_ok(ts[i]))
+                return TRA_ERR_INVALID;
+        if (LSE == nullptr || delta == nullptr)
+            return TRA_ERR_INVALID;
+    }
+    for (int i = 0; i < 8; ++i) {
+        const tra_tensor *t = ts[i];
+        if (t->B != Q->B || t->H != Q->H || t->N != Q->N || t->D != Q->D)
+            return TRA_ERR_SHAPE;
+        if (t->B < 0 || t->H < 0 || t->N < 0 || t->D < 0)
+            return TRA_ERR_SHAPE;
+    }
+    if (Q->N != mask->info.n)
+        return TRA_ERR_SHAPE;
+    for (int i = 0; i < 8; ++i)
+        if (ts[i]->dtype != TRA_BF16)
+            return TRA_ERR_UNSUPPORTED;
+    if (Q->D != 64 && Q->D != 128)
+        return TRA_ERR_UNSUPPORTED;
+    for (int i = 0; i < 8; ++i) {
+        const tra_tensor *t = ts[i];
+        if (t->stride[3] != 1)
+            return TRA_ERR_UNSUPPORTED;
+        for (int j = 0; j < 3; ++j)
+            if (t->stride[j] < 0 || t->stride[j] % 8 != 0)
+                return TRA_ERR_UNSUPPORTED;
+        if (((uintptr_t)t->data) % 16 != 0)
+            return TRA_ERR_UNSUPPORTED;
+    }
+    if (empty)
+        return TRA_OK;
+    if (Q->B * Q->H * mask->info.nqb >= ((int64_t)1 << 31) || Q->B * Q->H * Q->N >= ((int64_t)1 << 40))
+        return TRA_ERR_UNSUPPORTED;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_status(e);
+    if (dev != mask->device)
+        return TRA_ERR_INVALID;
+
+    tra::BwdArgs a;
+    std::memset(&a, 0, sizeof(a));
+    fill_attn_args(a.f, Q, K, V, nullptr, nullptr, mask, scale);
+    a.o = O->data;
+    a.dout = dO->data;
+    a.dq = dQ->data;
+    a.dk = dK->data;
+    a.dv = dV->data;
+    a.lse = LSE;
+    a.delta = delta;
+    for (int i = 0; i < 3; ++i) {
+        a.s_o[i] = O->stride[i];
+        a.s_do[i] = dO->stride[i];
+        a.s_dq[i] = dQ->stride[i];
+        a.s_dk[i] = dK->stride[i];
+        a.s_dv[i] = dV->stride[i];
+    }
+    return hip_status(tra::launch_attn_bwd_bf16(a, (hipStream_t)hip_stream));
+}
+
+}  // extern "C\"

@@ -55,6 +55,16 @@ struct MaskDev {
     uint32_t *queue;           // [kQueueWords] XCD queue counters, finished-group counter
     int32_t nqb;
     int32_t npairs;
+    // The same schedule over key blocks (columns of the block mask), for the
+    // kernels that accumulate per key block: pairs of key blocks whose query
+    // blocks largely coincide, and the merged query-block list of each pair
+    // with the emask index of block (query block, member key block).
+    const int32_t *t_pair_cols;   // [t_npairs][2] key blocks (second = -1: unpaired)
+    const int32_t *t_pair_ptr;    // [t_npairs + 1]
+    const int32_t *t_u_row;       // [t_nunion] query block
+    const int32_t *t_u_em;        // [t_nunion][2]
+    const int32_t *t_pair_order;  // [t_npairs]
+    int32_t t_npairs;
 };
 
 }  // namespace tra
@@ -77,6 +87,13 @@ struct tra_mask {
     int32_t *pair_order;
     int32_t npairs;
     uint32_t *queue;
+    int32_t *t_pair_cols;
+    int32_t *t_pair_ptr;
+    int32_t *t_u_row;
+    int32_t *t_u_em;
+    int32_t *t_pair_order;
+    int32_t t_npairs;
+    int64_t t_nunion;
 };
 
 namespace tra {
@@ -107,5 +124,17 @@ struct AttnArgs {
 };
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t st);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t st);
+
+// Attention backward (attn_bwd_bf16.hip): gradients of eq. 2 from the saved
+// LSE.  delta[row] = dO[row] . O[row] is computed first into a caller buffer.
+struct BwdArgs {
+    AttnArgs f;          // q, k, v, strides, shape, scale, mask (o unused)
+    const void *o, *dout;
+    void *dq, *dk, *dv;
+    const float *lse;
+    float *delta;
+    int64_t s_o[3], s_do[3], s_dq[3], s_dk[3], s_dv[3];
+};
+hipError_t launch_attn_bwd_bf16(const BwdArgs &a, hipStream_t st);
 
 }  // namespace tra
