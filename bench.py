@@ -119,6 +119,7 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=30.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 2 GiB device copy (counter calibration)")
@@ -218,6 +219,35 @@ def main():
                       "dense_tflops": round(dflops / (dense_ms * 1e-3) / 1e12, 2),
                       "speedup_vs_dense": round(dense_ms / launch_ms, 3)})
         dmask.free()
+
+    if not args.no_bwd and w.dtype == "bf16":
+        # backward (gradients from the saved LSE) on the same mask and inputs
+        bmask = tra.build_mask(w.f, w.s, w.kind, **w.mask_kwargs())
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.seed + 7)
+        dout = torch.randn(q.shape, generator=g, device=dev).to(torch.bfloat16)
+        tra.sparse_attn_fwd(q, k, v, bmask, out=out, lse=lse, stream=stream)
+        grads = tuple(torch.empty_like(q) for _ in range(3))
+        delta = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        tra.sparse_attn_bwd(q, k, v, out, lse, dout, bmask, grads=grads, delta=delta, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record(stream)
+        for _ in range(reps):
+            tra.sparse_attn_bwd(q, k, v, out, lse, dout, bmask, grads=grads, delta=delta, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = e0.elapsed_time(e1) / reps
+        extra.update({"bwd_ms": round(bwd_ms, 3),
+                      # 5 products per kept block (S, dP, dV, dK, dQ) is the usual accounting
+                      "bwd_tflops_5gemm": round(2.5 * flops_blocks / (bwd_ms * 1e-3) / 1e12, 2),
+                      # this build recomputes S and dP for dQ: 7 products are executed
+                      "bwd_mfma_tflops_7gemm": round(3.5 * flops_blocks / (bwd_ms * 1e-3) / 1e12, 2),
+                      "bwd_pct_bf16_peak_7gemm": round(100 * 3.5 * flops_blocks / (bwd_ms * 1e-3) / 1e12
+                                                       / BF16_PEAK_TFLOPS, 2)})
+        del grads, delta, dout
+        bmask.free()
 
     if not args.no_dense and name == workloads.HEADLINE:
         # second block reading on the same inputs: eq. 4 on block indices

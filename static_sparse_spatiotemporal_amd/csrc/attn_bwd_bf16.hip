@@ -213,7 +213,6 @@ void k_bwd_dkdv(BwdArgs a)
     const int N = f.N;
     const float c2 = f.scale_log2;
     const float scale = c2 / kLog2e;
-    const TileOffsets<D> off(lane);
 
     const int crow0 = wave * G::RPI + lane / G::CPR;
     const int cpc = lane % G::CPR;
@@ -286,6 +285,11 @@ void k_bwd_dkdv(BwdArgs a)
 #pragma unroll 1
             for (int c = 0; c < 4; ++c) {
                 const int cr = c * 32 * G::ROWB;
+                // fragment offsets are recomputed per chunk (a few VALU
+                // operations) instead of held in 16 registers across the loop
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                const TileOffsets<D> off(ln);
                 // ---- S = Q K^T and dP = dO V^T (32 queries x 32 keys) ----
                 f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
