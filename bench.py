@@ -249,6 +249,38 @@ def main():
         del grads, delta, dout
         bmask.free()
 
+    if w.kind == "swa" and w.dtype == "bf16" and w.s % 128 == 0:
+        # frame streaming through the K/V ring: steady state (ring full), one
+        # step = append the next frame's K, V + attention of its queries
+        cache = tra.KVCache(w.B, w.H, w.s, w.D, w.window)
+        fr = lambda x, i: x[:, :, (i % w.f) * w.s:(i % w.f + 1) * w.s]
+        fo = torch.empty_like(fr(q, 0))
+        flse = torch.empty(fo.shape[:3], dtype=torch.float32, device=dev)
+        for i in range(w.window):
+            cache.append(fr(k, i), fr(v, i), stream=stream)
+            cache.attn(fr(q, i), out=fo, lse=flse, stream=stream)
+        torch.cuda.synchronize()
+        reps = 20
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        for i in range(w.window, w.window + reps):
+            cache.append(fr(k, i), fr(v, i), stream=stream)
+            cache.attn(fr(q, i), out=fo, lse=flse, stream=stream)
+        e1.record(stream)
+        for i in range(reps):
+            cache.attn(fr(q, i), out=fo, lse=flse, stream=stream)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        step_ms = e0.elapsed_time(e1) / reps
+        attn_ms = e1.elapsed_time(e2) / reps
+        sflops = 4.0 * w.D * w.s * w.window * w.s * w.B * w.H
+        extra.update({"stream_window_frames": w.window,
+                      "stream_step_ms": round(step_ms, 4),
+                      "stream_attn_ms": round(attn_ms, 4),
+                      "stream_attn_tflops": round(sflops / (attn_ms * 1e-3) / 1e12, 2),
+                      "full_sequence_ms_per_frame": round(launch_ms / w.f, 4)})
+        cache.free()
+
     if not args.no_dense and name == workloads.HEADLINE:
         # second block reading on the same inputs: eq. 4 on block indices
         w2 = workloads.WORKLOADS["radial_f128_s1024_block_eq4"]

@@ -205,6 +205,44 @@ tra_status tra_sparse_attn_bwd(const tra_tensor *Q, const tra_tensor *K, const t
                                const tra_mask *mask, tra_tensor *dQ, tra_tensor *dK, tra_tensor *dV,
                                float *delta, float scale, void *hip_stream);
 
+/*
+ * Frame-streaming K/V cache for the frame sliding-window causal family (Vera
+ * 1.1 temporal module, section 3.1): keeps the keys and values of the last
+ * `window` frames in a ring; appending a frame evicts the oldest one once the
+ * ring is full.  tra_kvcache_attn then computes the rows of the newest frame
+ * of TRA_MASK_SWA_CAUSAL attention (query frame i over key frames
+ * max(0, i - window + 1) .. i) without the earlier frames' queries.
+ *
+ * tra_kvcache_create -- allocate the ring (2 x B x H x window x s x D bf16)
+ *   and a split workspace for B heads-batch, H heads, s tokens per frame
+ *   (a multiple of 128), head dim D in {64, 128}, dtype TRA_BF16.  Errors:
+ *   TRA_ERR_INVALID (null out, a size < 1), TRA_ERR_UNSUPPORTED (other dtype,
+ *   D, or s % 128 != 0), TRA_ERR_OOM, TRA_ERR_HIP.
+ * tra_kvcache_append -- copy K, V of the next frame ([B, H, s, D] views,
+ *   same rules as the attention tensors) into the ring (asynchronous on the
+ *   stream; the frame counter advances on the host).
+ * tra_kvcache_attn -- O = softmax(Q K^T * scale) V for Q, O [B, H, s, D] of
+ *   the newest frame over every cached frame; LSE as tra_sparse_attn_fwd (NULL
+ *   skips it).  The keys are split over workgroups and the partial results
+ *   merged (asynchronous; allocates nothing).  TRA_ERR_INVALID when nothing
+ *   has been appended.
+ * tra_kvcache_get_frames -- frames appended since creation/reset and frames
+ *   currently cached (<= window).
+ * tra_kvcache_reset -- start a new sequence (no device work).
+ * tra_kvcache_free -- release the cache (NULL is ignored); the caller makes
+ *   sure no call using it is still queued.
+ * Calls on one cache must not run concurrently.
+ */
+typedef struct tra_kvcache tra_kvcache;
+tra_status tra_kvcache_create(int64_t B, int64_t H, int64_t s, int64_t D, int32_t window, int32_t dtype,
+                              tra_kvcache **out);
+tra_status tra_kvcache_append(tra_kvcache *cache, const tra_tensor *K, const tra_tensor *V, void *hip_stream);
+tra_status tra_kvcache_attn(tra_kvcache *cache, const tra_tensor *Q, tra_tensor *O, float *LSE, float scale,
+                            void *hip_stream);
+tra_status tra_kvcache_get_frames(const tra_kvcache *cache, int64_t *appended, int64_t *cached);
+tra_status tra_kvcache_reset(tra_kvcache *cache);
+void tra_kvcache_free(tra_kvcache *cache);
+
 /* Copy the host-side summary filled at build time.  No device work. */
 tra_status tra_mask_get_info(const tra_mask *mask, tra_mask_info *out);
 

@@ -21,7 +21,7 @@ import os
 import numpy as np
 import torch
 
-__all__ = ["build_mask", "sparse_attn_fwd", "sparse_attn_bwd", "Mask", "TraError", "library_path", "load_library",
+__all__ = ["build_mask", "sparse_attn_fwd", "sparse_attn_bwd", "KVCache", "Mask", "TraError", "library_path", "load_library",
            "KINDS", "GRANULARITIES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -94,6 +94,19 @@ def load_library():
                                         P(TensorDesc), vp, vp, P(TensorDesc), P(TensorDesc), P(TensorDesc),
                                         vp, ctypes.c_float, vp]
     lib.tra_sparse_attn_bwd.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.tra_kvcache_create.argtypes = [i64, i64, i64, i64, ctypes.c_int32, ctypes.c_int32, P(vp)]
+    lib.tra_kvcache_create.restype = ctypes.c_int
+    lib.tra_kvcache_append.argtypes = [vp, P(TensorDesc), P(TensorDesc), vp]
+    lib.tra_kvcache_append.restype = ctypes.c_int
+    lib.tra_kvcache_attn.argtypes = [vp, P(TensorDesc), P(TensorDesc), vp, ctypes.c_float, vp]
+    lib.tra_kvcache_attn.restype = ctypes.c_int
+    lib.tra_kvcache_get_frames.argtypes = [vp, P(i64), P(i64)]
+    lib.tra_kvcache_get_frames.restype = ctypes.c_int
+    lib.tra_kvcache_reset.argtypes = [vp]
+    lib.tra_kvcache_reset.restype = ctypes.c_int
+    lib.tra_kvcache_free.argtypes = [vp]
+    lib.tra_kvcache_free.restype = None
     lib.tra_mask_get_info.argtypes = [vp, P(MaskInfo)]
     lib.tra_mask_get_info.restype = ctypes.c_int
     lib.tra_mask_export.argtypes = [vp, vp, vp, vp, vp, vp, vp]
@@ -250,3 +263,63 @@ def sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
         *(ctypes.byref(d) for d in gd), ctypes.c_void_p(delta.data_ptr()),
         float(scale) if scale else 0.0, _stream_handle(stream)), "tra_sparse_attn_bwd")
     return grads
+
+
+class KVCache:
+    """Frame-streaming K/V ring for the frame sliding-window causal mask (see
+    tra_kvcache_create).  append(k, v) adds the next frame ([B, H, s, D] bf16);
+    attn(q) returns (O, LSE) of that frame's queries over the cached frames."""
+
+    def __init__(self, B: int, H: int, s: int, D: int, window: int):
+        lib = load_library()
+        h = ctypes.c_void_p()
+        _check(lib.tra_kvcache_create(B, H, s, D, window, _BF16, ctypes.byref(h)), "tra_kvcache_create")
+        self._h = h
+        self.shape = (B, H, s, D)
+        self.window = window
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("cache was freed")
+        return self._h
+
+    def append(self, k: torch.Tensor, v: torch.Tensor, stream=None):
+        dk, dv = _desc(k), _desc(v)
+        _check(load_library().tra_kvcache_append(self.handle, ctypes.byref(dk), ctypes.byref(dv),
+                                                 _stream_handle(stream)), "tra_kvcache_append")
+
+    def attn(self, q: torch.Tensor, out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True,
+             scale: float | None = None, stream=None):
+        if out is None:
+            out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+        if lse is True:
+            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        elif lse is False:
+            lse = None
+        dq, do = _desc(q), _desc(out)
+        _check(load_library().tra_kvcache_attn(
+            self.handle, ctypes.byref(dq), ctypes.byref(do),
+            ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
+            float(scale) if scale else 0.0, _stream_handle(stream)), "tra_kvcache_attn")
+        return out, lse
+
+    def frames(self):
+        a, c = ctypes.c_int64(), ctypes.c_int64()
+        _check(load_library().tra_kvcache_get_frames(self.handle, ctypes.byref(a), ctypes.byref(c)),
+               "tra_kvcache_get_frames")
+        return a.value, c.value
+
+    def reset(self):
+        _check(load_library().tra_kvcache_reset(self.handle), "tra_kvcache_reset")
+
+    def free(self):
+        if self._h is not None:
+            load_library().tra_kvcache_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass

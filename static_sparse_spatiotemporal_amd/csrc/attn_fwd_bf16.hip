@@ -100,7 +100,7 @@ __device__ inline void copy_tile(const __bf16 *X, int64_t stride, int key0, int 
     }
 }
 
-template <int D>
+template <int D, bool STREAM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(AttnArgs a)
 {
@@ -150,12 +150,10 @@ void attn_fwd_bf16(AttnArgs a)
     cint *u_col = (cint *)a.mask.u_col;
     cint *u_em = (cint *)a.mask.u_em;
 
-    WorkQueue wq(a.mask.queue, a.mask.pair_order, a.mask.npairs, kPairChunk, a.B * a.H);
-    int wx = xcd_id(), wtries = 0, bh = 0, pair = 0;
-    while (wq.next(wx, wtries, &sItem, bh, pair)) {
-        const int row = pair_rows[2 * pair + half];  // -1: this half idles
+    // One work item: query block `row` of this half (-1: idle) over the key
+    // blocks of schedule entries u0 .. u1 - 1.
+    auto item = [&](int bh, int row, int u0, int u1, int split) {
         const bool active = row >= 0;
-        const int u0 = pair_ptr[pair], u1 = pair_ptr[pair + 1];
         const int b = bh / a.H, h = bh - b * a.H;
         const __bf16 *Qp = (const __bf16 *)a.q + b * a.sq[0] + h * a.sq[1];
         const __bf16 *Kp = (const __bf16 *)a.k + b * a.sk[0] + h * a.sk[1];
@@ -163,9 +161,10 @@ void attn_fwd_bf16(AttnArgs a)
         __bf16 *Op = (__bf16 *)a.o + b * a.so[0] + h * a.so[1];
         const int q0 = row * kBlock + w4 * 32;
 
+        auto kcol = [&](int u) { return STREAM ? u : u_col[u]; };
         if (u0 < u1) {
-            copy_tile<D>(Kp, a.sk[2], u_col[u0] * kBlock, N, lK, wave, crow0, colK, offK);
-            copy_tile<D>(Vp, a.sv[2], u_col[u0] * kBlock, N, lV, wave, crow0, colV, offV);
+            copy_tile<D>(Kp, a.sk[2], kcol(u0) * kBlock, a.Nk, lK, wave, crow0, colK, offK);
+            copy_tile<D>(Vp, a.sv[2], kcol(u0) * kBlock, a.Nk, lV, wave, crow0, colV, offV);
         }
         bf16x8 qf[G::NKS];
         if (active) {
@@ -188,10 +187,10 @@ void attn_fwd_bf16(AttnArgs a)
             __syncthreads();
             if (u + 1 < u1) {
                 const int nb = buf ^ 1;
-                copy_tile<D>(Kp, a.sk[2], u_col[u + 1] * kBlock, N, lK + nb * G::TILE, wave, crow0, colK, offK);
-                copy_tile<D>(Vp, a.sv[2], u_col[u + 1] * kBlock, N, lV + nb * G::TILE, wave, crow0, colV, offV);
+                copy_tile<D>(Kp, a.sk[2], kcol(u + 1) * kBlock, a.Nk, lK + nb * G::TILE, wave, crow0, colK, offK);
+                copy_tile<D>(Vp, a.sv[2], kcol(u + 1) * kBlock, a.Nk, lV + nb * G::TILE, wave, crow0, colV, offV);
             }
-            const int em = active ? u_em[2 * u + half] : kAbsent;
+            const int em = active ? (STREAM ? -1 : u_em[2 * u + half]) : kAbsent;
             if (em == kAbsent)
                 continue;
             const char LDS_AS *tK = lK + buf * G::TILE;
@@ -295,7 +294,28 @@ void attn_fwd_bf16(AttnArgs a)
         }
 
         // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l) ----
-        if (active) {
+        if (STREAM && active) {
+            // normalised partial output and log2-sum-exp of this key split
+            const float lt = lane_pair_sum(l);
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            const int q = q0 + lq;
+            if (q < N) {
+                const int64_t r = ((int64_t)split * a.B * a.H + bh) * N + q;
+                float *prow = a.part_o + r * D;
+#pragma unroll
+                for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                        f32x4 v;
+#pragma unroll
+                        for (int x = 0; x < 4; ++x)
+                            v[x] = o[db][4 * i4 + x] * inv;
+                        *(f32x4 *)(prow + db * 32 + 8 * i4 + 4 * hh) = v;
+                    }
+                if (hh == 0)
+                    a.part_lse[r] = lt > 0.f ? m + __log2f(lt) : kNegInf;
+            }
+        } else if (active) {
             const float lt = lane_pair_sum(l);
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
             const int q = q0 + lq;
@@ -315,8 +335,86 @@ void attn_fwd_bf16(AttnArgs a)
                     a.lse[(int64_t)bh * N + q] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
             }
         }
+    };
+
+    if constexpr (STREAM) {
+        const int it = blockIdx.x;
+        const int split = it % a.nsplit, rest = it / a.nsplit;
+        const int pair = rest % a.stream_pairs, bh = rest / a.stream_pairs;
+        const int row = 2 * pair + half < a.mask.nqb ? 2 * pair + half : -1;
+        const int u0 = split * a.split_tiles;
+        const int u1 = u0 + a.split_tiles < a.nkv_tiles ? u0 + a.split_tiles : a.nkv_tiles;
+        item(bh, row, u0, u1, split);
+    } else {
+        WorkQueue wq(a.mask.queue, a.mask.pair_order, a.mask.npairs, kPairChunk, a.B * a.H);
+        int wx = xcd_id(), wtries = 0, bh = 0, pair = 0;
+        while (wq.next(wx, wtries, &sItem, bh, pair))
+            item(bh, pair_rows[2 * pair + half], pair_ptr[pair], pair_ptr[pair + 1], 0);
+        retire_group(a.mask.queue);
     }
-    retire_group(a.mask.queue);
+}
+
+// Merge of the key splits: per row, LSE2 = log2 sum_x 2^lse2_x and
+// O = sum_x 2^(lse2_x - LSE2) O_x.  8 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void k_merge_splits(AttnArgs a)
+{
+    constexpr int PER = D / 8;
+    const int64_t rows = (int64_t)a.B * a.H * a.N;
+    const int64_t r = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+    const int part = threadIdx.x & 7;
+    if (r >= rows)
+        return;
+    float mx = kNegInf;
+    for (int x = 0; x < a.nsplit; ++x)
+        mx = fmaxf(mx, a.part_lse[(int64_t)x * rows + r]);
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+        acc[e] = 0.f;
+    float tot = 0.f;
+    for (int x = 0; x < a.nsplit; ++x) {
+        const float w = __builtin_amdgcn_exp2f(a.part_lse[(int64_t)x * rows + r] - mx);
+        tot += w;
+        const float *po = a.part_o + ((int64_t)x * rows + r) * D + part * PER;
+#pragma unroll
+        for (int e = 0; e < PER; e += 4) {
+            const f32x4 v = *(const f32x4 *)(po + e);
+#pragma unroll
+            for (int y = 0; y < 4; ++y)
+                acc[e + y] = fmaf(w, v[y], acc[e + y]);
+        }
+    }
+    const float inv = 1.f / tot;
+    const int64_t bh = r / a.N, q = r - bh * a.N;
+    const int64_t b = bh / a.H, h = bh - b * a.H;
+    __bf16 *orow = (__bf16 *)a.o + b * a.so[0] + h * a.so[1] + q * a.so[2] + part * PER;
+#pragma unroll
+    for (int e = 0; e < PER; e += 8) {
+        f32x8 v;
+#pragma unroll
+        for (int y = 0; y < 8; ++y)
+            v[y] = acc[e + y] * inv;
+        *(bf16x8 *)(orow + e) = __builtin_convertvector(v, bf16x8);
+    }
+    if (a.lse && part == 0)
+        a.lse[r] = (mx + __log2f(tot)) * kLn2;
+}
+
+// dst[b, h, row0 + r, :] = src[b, h, r, :]; one 16-byte chunk per thread.
+__global__ __launch_bounds__(256) void k_ring_copy(const __bf16 *src, int64_t s0, int64_t s1, int64_t s2,
+                                                  __bf16 *ring, int64_t H, int64_t rows, int64_t D,
+                                                  int64_t ring_rows, int64_t row0, int64_t total)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= total)
+        return;
+    const int64_t cpr = D / 8;
+    const int64_t c = t % cpr, rr = t / cpr;
+    const int64_t r = rr % rows, bh = rr / rows;
+    const int64_t b = bh / H, h = bh - b * H;
+    const bf16x8 v = *(const bf16x8 *)(src + b * s0 + h * s1 + r * s2 + 8 * c);
+    *(bf16x8 *)(ring + (bh * ring_rows + row0 + r) * D + 8 * c) = v;
 }
 
 }  // namespace
@@ -324,8 +422,38 @@ void attn_fwd_bf16(AttnArgs a)
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t st)
 {
     const long long items = (long long)a.B * a.H * a.mask.npairs;
-    return a.D == 128 ? launch_persistent(attn_fwd_bf16<128>, kThreads, items, a, st)
-                      : launch_persistent(attn_fwd_bf16<64>, kThreads, items, a, st);
+    return a.D == 128 ? launch_persistent(attn_fwd_bf16<128, false>, kThreads, items, a, st)
+                      : launch_persistent(attn_fwd_bf16<64, false>, kThreads, items, a, st);
+}
+
+hipError_t launch_attn_stream_bf16(const AttnArgs &a, hipStream_t st)
+{
+    const long long items = (long long)a.B * a.H * a.stream_pairs * a.nsplit;
+    if (a.D == 128)
+        hipLaunchKernelGGL((attn_fwd_bf16<128, true>), dim3((unsigned)items), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((attn_fwd_bf16<64, true>), dim3((unsigned)items), dim3(kThreads), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const long long rows = (long long)a.B * a.H * a.N;
+    const unsigned grid = (unsigned)((rows + 31) / 32);
+    if (a.D == 128)
+        hipLaunchKernelGGL(k_merge_splits<128>, dim3(grid), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_merge_splits<64>, dim3(grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_ring_copy(const void *src, const int64_t *s_src, void *ring, int64_t B, int64_t H, int64_t rows,
+                            int64_t D, int64_t ring_rows, int64_t row0, hipStream_t st)
+{
+    const int64_t total = B * H * rows * (D / 8);
+    if (total == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_ring_copy, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, (const __bf16 *)src,
+                       s_src[0], s_src[1], s_src[2], (__bf16 *)ring, H, rows, D, ring_rows, row0, total);
+    return hipGetLastError();
 }
 
 }  // namespace tra

@@ -183,9 +183,24 @@ void fill_attn_args(tra::AttnArgs &a, const tra_tensor *Q, const tra_tensor *K, 
     a.mask.t_u_em = mask->t_u_em;
     a.mask.t_pair_order = mask->t_pair_order;
     a.mask.t_npairs = mask->t_npairs;
+    a.Nk = a.N;
+    a.part_o = nullptr;
+    a.part_lse = nullptr;
+    a.nsplit = a.split_tiles = a.nkv_tiles = a.stream_pairs = 0;
 }
 
 }  // namespace
+
+// Frame-streaming K/V cache (see tra_kvcache_create).
+struct tra_kvcache {
+    int64_t B, H, s, D;
+    int32_t window;
+    int device;
+    int64_t appended;  // frames appended since creation or reset
+    int32_t nsplit_max;
+    __bf16 *ring_k, *ring_v;  // [B, H, window * s, D]
+    float *part_o, *part_lse;
+};
 
 extern "C" {
 
@@ -611,4 +626,180 @@ tra_status tra_sparse_attn_bwd(const tra_tensor *Q, const tra_tensor *K, const t
     return hip_status(tra::launch_attn_bwd_bf16(a, (hipStream_t)hip_stream));
 }
 
-}  // extern "C\"
+tra_status tra_kvcache_create(int64_t B, int64_t H, int64_t s, int64_t D, int32_t window, int32_t dtype,
+                              tra_kvcache **out)
+{
+    if (out == nullptr)
+        return TRA_ERR_INVALID;
+    *out = nullptr;
+    if (B < 1 || H < 1 || s < 1 || window < 1)
+        return TRA_ERR_INVALID;
+    if (dtype != TRA_BF16 || (D != 64 && D != 128) || s % tra::kBlock != 0)
+        return TRA_ERR_UNSUPPORTED;
+    const int64_t ring_rows = (int64_t)window * s;
+    if (ring_rows >= ((int64_t)1 << 31) || B * H * ring_rows >= ((int64_t)1 << 40))
+        return TRA_ERR_UNSUPPORTED;
+    tra_kvcache *c = new (std::nothrow) tra_kvcache;
+    if (c == nullptr)
+        return TRA_ERR_OOM;
+    std::memset(c, 0, sizeof(*c));
+    c->B = B;
+    c->H = H;
+    c->s = s;
+    c->D = D;
+    c->window = window;
+    c->nsplit_max = (int32_t)(ring_rows / tra::kBlock);
+    const size_t ring = (size_t)(B * H * ring_rows * D);
+    const size_t rows = (size_t)(B * H * s);
+    tra_status st_ = TRA_OK;
+    TRA_HIP(hipGetDevice(&c->device));
+    TRA_HIP(dev_alloc(&c->ring_k, ring));
+    TRA_HIP(dev_alloc(&c->ring_v, ring));
+    TRA_HIP(dev_alloc(&c->part_o, (size_t)c->nsplit_max * rows * D));
+    TRA_HIP(dev_alloc(&c->part_lse, (size_t)c->nsplit_max * rows));
+    *out = c;
+    return TRA_OK;
+fail:
+    (void)hipFree(c->ring_k);
+    (void)hipFree(c->ring_v);
+    (void)hipFree(c->part_o);
+    (void)hipFree(c->part_lse);
+    delete c;
+    return st_;
+}
+
+static tra_status check_frame_tensor(const tra_kvcache *c, const tra_tensor *t)
+{
+    if (t == nullptr || t->data == nullptr)
+        return TRA_ERR_INVALID;
+    if (t->B != c->B || t->H != c->H || t->N != c->s || t->D != c->D)
+        return TRA_ERR_SHAPE;
+    if (t->dtype != TRA_BF16)
+        return TRA_ERR_UNSUPPORTED;
+    if (t->stride[3] != 1)
+        return TRA_ERR_UNSUPPORTED;
+    for (int j = 0; j < 3; ++j)
+        if (t->stride[j] < 0 || t->stride[j] % 8 != 0)
+            return TRA_ERR_UNSUPPORTED;
+    if (((uintptr_t)t->data) % 16 != 0)
+        return TRA_ERR_UNSUPPORTED;
+    return TRA_OK;
+}
+
+static tra_status check_device(const tra_kvcache *c)
+{
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_status(e);
+    return dev == c->device ? TRA_OK : TRA_ERR_INVALID;
+}
+
+tra_status tra_kvcache_append(tra_kvcache *c, const tra_tensor *K, const tra_tensor *V, void *hip_stream)
+{
+    if (c == nullptr)
+        return TRA_ERR_INVALID;
+    tra_status st = check_frame_tensor(c, K);
+    if (st == TRA_OK)
+        st = check_frame_tensor(c, V);
+    if (st == TRA_OK)
+        st = check_device(c);
+    if (st != TRA_OK)
+        return st;
+    const int64_t ring_rows = (int64_t)c->window * c->s;
+    const int64_t row0 = (c->appended % c->window) * c->s;
+    hipStream_t hs = (hipStream_t)hip_stream;
+    hipError_t e = tra::launch_ring_copy(K->data, K->stride, c->ring_k, c->B, c->H, c->s, c->D, ring_rows, row0, hs);
+    if (e == hipSuccess)
+        e = tra::launch_ring_copy(V->data, V->stride, c->ring_v, c->B, c->H, c->s, c->D, ring_rows, row0, hs);
+    if (e != hipSuccess)
+        return hip_status(e);
+    c->appended++;
+    return TRA_OK;
+}
+
+tra_status tra_kvcache_attn(tra_kvcache *c, const tra_tensor *Q, tra_tensor *O, float *LSE, float scale,
+                            void *hip_stream)
+{
+    if (c == nullptr)
+        return TRA_ERR_INVALID;
+    tra_status st = check_frame_tensor(c, Q);
+    if (st == TRA_OK)
+        st = check_frame_tensor(c, O);
+    if (st == TRA_OK)
+        st = check_device(c);
+    if (st != TRA_OK)
+        return st;
+    if (c->appended == 0)
+        return TRA_ERR_INVALID;
+    const int64_t frames = std::min<int64_t>(c->appended, c->window);
+    const int64_t ring_rows = (int64_t)c->window * c->s;
+
+    tra::AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = Q->data;
+    a.k = c->ring_k;
+    a.v = c->ring_v;
+    a.o = O->data;
+    a.lse = LSE;
+    for (int i = 0; i < 3; ++i) {
+        a.sq[i] = Q->stride[i];
+        a.so[i] = O->stride[i];
+    }
+    a.sk[0] = a.sv[0] = c->H * ring_rows * c->D;
+    a.sk[1] = a.sv[1] = ring_rows * c->D;
+    a.sk[2] = a.sv[2] = c->D;
+    a.B = (int32_t)c->B;
+    a.H = (int32_t)c->H;
+    a.N = (int32_t)c->s;
+    a.Nk = (int32_t)ring_rows;
+    a.D = (int32_t)c->D;
+    const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)c->D);
+    a.scale_log2 = (float)(sc * 1.4426950408889634);
+    a.mask.nqb = (int32_t)(c->s / tra::kBlock);
+    a.stream_pairs = (a.mask.nqb + 1) / 2;
+    a.nkv_tiles = (int32_t)(frames * c->s / tra::kBlock);
+    // about two workgroups per compute unit, at least one key tile each
+    int cus = 256;
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->device);
+    const int64_t base = c->B * c->H * a.stream_pairs;
+    int64_t want = (2 * (int64_t)cus + base - 1) / base;
+    want = std::max<int64_t>(1, std::min<int64_t>(want, a.nkv_tiles));
+    a.split_tiles = (int32_t)((a.nkv_tiles + want - 1) / want);
+    a.nsplit = (a.nkv_tiles + a.split_tiles - 1) / a.split_tiles;
+    a.part_o = c->part_o;
+    a.part_lse = c->part_lse;
+    return hip_status(tra::launch_attn_stream_bf16(a, (hipStream_t)hip_stream));
+}
+
+tra_status tra_kvcache_get_frames(const tra_kvcache *c, int64_t *appended, int64_t *cached)
+{
+    if (c == nullptr)
+        return TRA_ERR_INVALID;
+    if (appended)
+        *appended = c->appended;
+    if (cached)
+        *cached = std::min<int64_t>(c->appended, c->window);
+    return TRA_OK;
+}
+
+tra_status tra_kvcache_reset(tra_kvcache *c)
+{
+    if (c == nullptr)
+        return TRA_ERR_INVALID;
+    c->appended = 0;
+    return TRA_OK;
+}
+
+void tra_kvcache_free(tra_kvcache *c)
+{
+    if (c == nullptr)
+        return;
+    (void)hipFree(c->ring_k);
+    (void)hipFree(c->ring_v);
+    (void)hipFree(c->part_o);
+    (void)hipFree(c->part_lse);
+    delete c;
+}
+
+}  // extern "C"

@@ -121,8 +121,23 @@ struct AttnArgs {
     int32_t B, H, N, D;
     float scale_log2;  // scale * log2(e)
     MaskDev mask;
+    // Key rows (copies past Nk repeat row Nk - 1); N for the masked call.
+    int32_t Nk;
+    // Split-key mode (frame streaming over a K/V ring): query blocks are
+    // paired in order, every key block in [0, nkv_tiles) is kept whole, and
+    // split x of the key blocks writes its normalised partial output and
+    // log2-sum-exp to part_o / part_lse, merged by a second kernel.
+    float *part_o;     // [nsplit][B * H * N][D]
+    float *part_lse;   // [nsplit][B * H * N]
+    int32_t nsplit, split_tiles, nkv_tiles, stream_pairs;
 };
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t st);
+// Split-key launch (see AttnArgs) followed by the merge into a.o / a.lse.
+hipError_t launch_attn_stream_bf16(const AttnArgs &a, hipStream_t st);
+// Copy a [B, H, rows, D] bf16 view into rows row0 .. of a contiguous
+// [B, H, ring_rows, D] buffer.
+hipError_t launch_ring_copy(const void *src, const int64_t *s_src, void *ring, int64_t B, int64_t H, int64_t rows,
+                            int64_t D, int64_t ring_rows, int64_t row0, hipStream_t st);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t st);
 
 // Attention backward (attn_bwd_bf16.hip): gradients of eq. 2 from the saved
