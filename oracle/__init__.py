@@ -84,6 +84,10 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             P(_Mask), ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.orc_linear_attention_rows.argtypes = [
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int]
         lib.orc_row_counts.argtypes = [P(_Mask), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_void_p]
         lib.orc_attention_rows.argtypes = [
@@ -294,3 +298,30 @@ def attention_bwd_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.nda
                                    k_rows.ctypes.data, k_rows.shape[0], dk.ctypes.data, dv.ctypes.data,
                                    threads or default_threads())
     return dq, dk, dv
+
+
+def linear_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.ndarray | None = None,
+                          eps: float = 1e-6, threads: int | None = None) -> np.ndarray:
+    """fp64 ReLU-kernel linear attention (SALAD linear branch) for selected rows.
+
+    Arrays as attention_rows; every key of the (b, h) counts.  Returns O
+    [nrows, d] float64.
+    """
+    B, H, n, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    if q.dtype == np.float32:
+        dtype = F32
+    elif q.dtype == np.uint16:
+        dtype = BF16
+    else:
+        raise TypeError("q/k/v must be float32 or uint16 (bfloat16 bits)")
+    q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+    if rows is None:
+        bb, hh, qq = np.meshgrid(np.arange(B), np.arange(H), np.arange(n), indexing="ij")
+        rows = np.stack([bb.ravel(), hh.ravel(), qq.ravel()], axis=1)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    o = np.zeros((rows.shape[0], d), dtype=np.float64)
+    _load().orc_linear_attention_rows(dtype, q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, n, d,
+                                      float(eps), rows.ctypes.data, rows.shape[0], o.ctypes.data,
+                                      threads or default_threads())
+    return o

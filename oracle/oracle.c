@@ -618,3 +618,81 @@ void orc_attention_bwd_rows(int dtype, const void *q, const void *k, const void 
     free(keys);
     free(tid);
 }
+
+/* ---- SALAD linear branch ------------------------------------------------- */
+
+typedef struct {
+    int dtype;
+    const void *q, *k, *v;
+    int64_t H, n, d;
+    double eps;
+    const int64_t *rows;
+    int64_t begin, end;
+    double *o_out;
+} lin_job;
+
+static double relu(double x) { return x > 0.0 ? x : 0.0; }
+
+static void *lin_worker(void *arg)
+{
+    lin_job *j = (lin_job *)arg;
+    const int64_t n = j->n, d = j->d;
+    double *fq = (double *)malloc((size_t)d * sizeof(double));
+    for (int64_t r = j->begin; r < j->end; r++) {
+        int64_t b = j->rows[3 * r], h = j->rows[3 * r + 1], q = j->rows[3 * r + 2];
+        int64_t head = (b * j->H + h) * n * d;
+        double *o = j->o_out + r * d;
+        for (int64_t x = 0; x < d; x++) {
+            fq[x] = relu(load_value(j->dtype, j->q, head + q * d + x));
+            o[x] = 0.0;
+        }
+        double wsum = 0.0;
+        for (int64_t t = 0; t < n; t++) {
+            double w = 0.0;
+            for (int64_t x = 0; x < d; x++)
+                w += fq[x] * relu(load_value(j->dtype, j->k, head + t * d + x));
+            if (w == 0.0)
+                continue;
+            wsum += w;
+            for (int64_t x = 0; x < d; x++)
+                o[x] += w * load_value(j->dtype, j->v, head + t * d + x);
+        }
+        for (int64_t x = 0; x < d; x++)
+            o[x] /= wsum + j->eps;
+    }
+    free(fq);
+    return NULL;
+}
+
+void orc_linear_attention_rows(int dtype, const void *q, const void *k, const void *v, int64_t B, int64_t H,
+                               int64_t n, int64_t d, double eps, const int64_t *rows, int64_t nrows,
+                               double *o_out, int threads)
+{
+    (void)B;
+    if (threads < 1)
+        threads = 1;
+    if (threads > nrows)
+        threads = nrows > 0 ? (int)nrows : 1;
+    lin_job *jobs = (lin_job *)calloc((size_t)threads, sizeof(lin_job));
+    pthread_t *tid = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    for (int w = 0; w < threads; w++) {
+        lin_job *j = &jobs[w];
+        j->dtype = dtype;
+        j->q = q;
+        j->k = k;
+        j->v = v;
+        j->H = H;
+        j->n = n;
+        j->d = d;
+        j->eps = eps;
+        j->rows = rows;
+        j->begin = nrows * w / threads;
+        j->end = nrows * (w + 1) / threads;
+        j->o_out = o_out;
+        pthread_create(&tid[w], NULL, lin_worker, j);
+    }
+    for (int w = 0; w < threads; w++)
+        pthread_join(tid[w], NULL);
+    free(jobs);
+    free(tid);
+}

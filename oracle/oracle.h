@@ -133,6 +133,17 @@ void orc_attention_bwd_rows(int dtype, const void *q, const void *k, const void 
                             const int64_t *k_rows, int64_t nk, double *dk_out, double *dv_out,
                             int threads);
 
+/* SALAD linear branch (page "SALAD", section 2.1): ReLU-kernel linear
+ * attention over the same Q, K, V, for a list of rows.  With phi = ReLU and
+ * w_t = phi(Q[q]) . phi(K[t]) over every key t of the (b, h):
+ *   O[q] = sum_t w_t V[t] / (sum_t w_t + eps)
+ * (the attention form; a linear-time kernel evaluates it as
+ * phi(Q) (phi(K)^T V) / (phi(Q) . sum_t phi(K[t]) + eps)).
+ * Layout and dtypes as orc_attention_rows. */
+void orc_linear_attention_rows(int dtype, const void *q, const void *k, const void *v, int64_t B, int64_t H,
+                               int64_t n, int64_t d, double eps, const int64_t *rows, int64_t nrows,
+                               double *o_out, int threads);
+
 #ifdef __cplusplus
 }
 #endif
