@@ -249,6 +249,26 @@ def main():
         del grads, delta, dout
         bmask.free()
 
+    if not args.no_bwd and w.dtype == "bf16" and name == workloads.HEADLINE:
+        # SALAD linear branch on the same Q, K, V (HBM-bound: Q, K, V read once, O written once)
+        lout = torch.empty_like(q)
+        lws = torch.empty(tra.linear_attn_workspace_bytes(*q.shape), dtype=torch.uint8, device=dev)
+        tra.linear_attn_fwd(q, k, v, out=lout, workspace=lws, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            tra.linear_attn_fwd(q, k, v, out=lout, workspace=lws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        lin_ms = e0.elapsed_time(e1) / reps
+        lbytes = 4 * q.numel() * q.element_size()
+        extra.update({"linear_branch_ms": round(lin_ms, 4),
+                      "linear_branch_gbs": round(lbytes / (lin_ms * 1e-3) / 1e9, 1),
+                      "linear_branch_pct_hbm": round(100 * lbytes / (lin_ms * 1e-3) / 8e12, 2)})
+        del lout, lws
+
     if w.kind == "swa" and w.dtype == "bf16" and w.s % 128 == 0:
         # frame streaming through the K/V ring: steady state (ring full), one
         # step = append the next frame's K, V + attention of its queries

@@ -53,6 +53,7 @@
 #ifndef TRA_H
 #define TRA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -242,6 +243,30 @@ tra_status tra_kvcache_attn(tra_kvcache *cache, const tra_tensor *Q, tra_tensor 
 tra_status tra_kvcache_get_frames(const tra_kvcache *cache, int64_t *appended, int64_t *cached);
 tra_status tra_kvcache_reset(tra_kvcache *cache);
 void tra_kvcache_free(tra_kvcache *cache);
+
+/*
+ * SALAD linear branch (page "SALAD", section 2.1): ReLU-kernel linear
+ * attention over the same Q, K, V as the sparse branch, for every row of
+ * every (b, h):
+ *     O[q] = phi(Q[q]) (sum_t phi(K[t])^T V[t]) / (phi(Q[q]) . sum_t phi(K[t]) + eps),
+ * phi = ReLU, O(N D^2) work.  The gate and the output projection of the
+ * branch are trained layers of the model around this call.
+ *
+ * tra_linear_attn_workspace_bytes -- bytes of device workspace the call
+ *   needs for [B, H, N, D] (0 for an unsupported D).
+ * tra_linear_attn_fwd -- Q, K, V, O: [B, H, N, D] bf16 views (forward's
+ *   rules; any N >= 1), eps >= 0 (1e-6 is typical), workspace: device
+ *   memory of at least that many bytes, 256-byte aligned, owned by the
+ *   caller and overwritten.  Accumulation in fp32; the d x d summary is
+ *   applied as a pair of bf16 values (about 16 significant bits); O rounded
+ *   to bf16.  Asynchronous; allocates nothing.  Errors: TRA_ERR_INVALID
+ *   (null tensor/data/workspace, workspace too small or misaligned,
+ *   eps < 0), TRA_ERR_SHAPE, TRA_ERR_UNSUPPORTED (dtype, D, stride or
+ *   alignment), TRA_ERR_HIP.
+ */
+size_t tra_linear_attn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
+tra_status tra_linear_attn_fwd(const tra_tensor *Q, const tra_tensor *K, const tra_tensor *V, tra_tensor *O,
+                               float eps, void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* Copy the host-side summary filled at build time.  No device work. */
 tra_status tra_mask_get_info(const tra_mask *mask, tra_mask_info *out);

@@ -21,7 +21,7 @@ import os
 import numpy as np
 import torch
 
-__all__ = ["build_mask", "sparse_attn_fwd", "sparse_attn_bwd", "KVCache", "Mask", "TraError", "library_path", "load_library",
+__all__ = ["build_mask", "sparse_attn_fwd", "sparse_attn_bwd", "linear_attn_fwd", "KVCache", "Mask", "TraError", "library_path", "load_library",
            "KINDS", "GRANULARITIES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +95,11 @@ def load_library():
                                         vp, ctypes.c_float, vp]
     lib.tra_sparse_attn_bwd.restype = ctypes.c_int
     i64 = ctypes.c_int64
+    lib.tra_linear_attn_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.tra_linear_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.tra_linear_attn_fwd.argtypes = [P(TensorDesc), P(TensorDesc), P(TensorDesc), P(TensorDesc),
+                                        ctypes.c_float, vp, ctypes.c_size_t, vp]
+    lib.tra_linear_attn_fwd.restype = ctypes.c_int
     lib.tra_kvcache_create.argtypes = [i64, i64, i64, i64, ctypes.c_int32, ctypes.c_int32, P(vp)]
     lib.tra_kvcache_create.restype = ctypes.c_int
     lib.tra_kvcache_append.argtypes = [vp, P(TensorDesc), P(TensorDesc), vp]
@@ -323,3 +328,28 @@ class KVCache:
             self.free()
         except Exception:
             pass
+
+
+def linear_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None,
+                    eps: float = 1e-6, workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """SALAD ReLU-kernel linear attention on the GPU (see tra_linear_attn_fwd).
+
+    q, k, v: [B, H, n, D] bf16 cuda tensors.  `workspace` (uint8 cuda tensor of
+    at least linear_attn_workspace_bytes bytes) defaults to a new one.
+    """
+    lib = load_library()
+    B, H, n, D = q.shape
+    need = int(lib.tra_linear_attn_workspace_bytes(B, H, n, D))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    descs = [_desc(t) for t in (q, k, v, out)]
+    _check(lib.tra_linear_attn_fwd(*(ctypes.byref(d) for d in descs), float(eps),
+                                   ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                   _stream_handle(stream)), "tra_linear_attn_fwd")
+    return out
+
+
+def linear_attn_workspace_bytes(B: int, H: int, n: int, D: int) -> int:
+    return int(load_library().tra_linear_attn_workspace_bytes(B, H, n, D))

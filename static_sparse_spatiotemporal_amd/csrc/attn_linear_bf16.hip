@@ -1,0 +1,352 @@
+// SALAD linear branch (page "SALAD", section 2.1) for gfx950: ReLU-kernel
+// linear attention over the same Q, K, V as the sparse branch,
+//   O = phi(Q) (phi(K)^T V) / (phi(Q) . sum_t phi(K_t) + eps),  phi = ReLU,
+// in O(N d^2) per (batch, head).  Three kernels:
+//   k_lin_reduce   one workgroup per (b, h, chunk of 2048 rows): KV^T =
+//                  V^T phi(K) (d x d, fp32) and z = sum_t phi(K_t) over its
+//                  rows with 32x32x16 bf16 MFMAs; both operands are read
+//                  transposed (ds_read_b64_tr_b16) from double-buffered
+//                  K/V tiles;
+//   k_lin_combine  sums the chunks, stores KV^T as a bf16 pair (hi + lo,
+//                  about 16 significant bits) and z in fp32;
+//   k_lin_apply    one workgroup per 256 queries: O^T = KV^T phi(Q)^T with
+//                  phi(Q) as the register B operand (two MFMAs per step for
+//                  hi and lo), the denominator phi(Q) . z per lane.
+// The path is HBM-bound (Q, K, V read once, O written once).
+#include "attn_common.h"
+
+namespace tra {
+namespace {
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kLinThreads = 512;  // 8 waves
+constexpr int kLinChunk = 2048;   // rows per reduce workgroup
+
+template <int D>
+struct LGeo {
+    static constexpr int ROWB = D * 2;
+    static constexpr int TILE = kBlock * ROWB;
+    static constexpr int CPR = D / 8;
+    static constexpr int RPI = 64 / CPR;
+    static constexpr int NCOPY = kBlock * CPR / kLinThreads;
+    static constexpr int NKS = D / 16;
+    static constexpr int NDB = D / 32;
+};
+
+template <int D>
+__device__ inline int lswz(int row)
+{
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+
+// Copy a 128-row tile (rows row0 .., clamped to N - 1) of X into LDS.
+template <int D>
+__device__ inline void lcopy_tile(const __bf16 *X, int64_t stride, int row0, int N, char LDS_AS *dst, int wave,
+                                  int lane)
+{
+    using G = LGeo<D>;
+    const int crow0 = wave * G::RPI + lane / G::CPR;
+    const int col = ((lane % G::CPR) ^ lswz<D>(crow0)) * 8;
+#pragma unroll
+    for (int i = 0; i < G::NCOPY; ++i) {
+        int r = row0 + crow0 + 8 * G::RPI * i;
+        r = r < N ? r : N - 1;
+        __builtin_amdgcn_global_load_lds((const void *)(X + (int64_t)r * stride + col),
+                                         (void LDS_AS *)(dst + (8 * i + wave) * 1024), 16, 0, 0);
+    }
+}
+
+// Transposed operand: 32 columns (block cb) x 16 rows 16 t + {8 (j / 4) +
+// 4 (lane / 32) + j % 4}, j = 0 .. 7.
+template <int D>
+__device__ inline bf16x8 ltr(const char LDS_AS *tile, int lane, int t, int cb)
+{
+    using G = LGeo<D>;
+    const int hh = lane >> 5, g = lane >> 4, r16 = lane & 15;
+    const int ra = 16 * t + 4 * hh + (r16 >> 2);
+    const int d = cb * 32 + (g & 1) * 16 + 4 * (r16 & 3);
+    const int o0 = ra * G::ROWB + (((d >> 3) ^ lswz<D>(ra)) << 4) + ((d & 7) << 1);
+    const int o1 = (ra + 8) * G::ROWB + (((d >> 3) ^ lswz<D>(ra + 8)) << 4) + ((d & 7) << 1);
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(tile + o0));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(tile + o1));
+    return __builtin_shufflevector(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b), 0, 1, 2, 3, 4, 5,
+                                   6, 7);
+}
+
+typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+
+// ReLU of 8 bf16 values (sign-magnitude: negative patterns are negative as
+// int16, so an integer max with 0 clears them).
+__device__ inline bf16x8 relu8(bf16x8 x)
+{
+    i16x8 v = __builtin_bit_cast(i16x8, x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        v[j] = v[j] > 0 ? v[j] : (short)0;
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+struct LinArgs {
+    const void *q, *k, *v;
+    void *o;
+    int64_t sq[3], sk[3], sv[3], so[3];
+    int32_t B, H, N, D, nchunk;
+    float eps;
+    float *part;      // [B * H * nchunk][D * D + D]: KV^T (dv-major) then z
+    __bf16 *kv_hi;    // [B * H][D][D] KV^T
+    __bf16 *kv_lo;    // [B * H][D][D] KV^T - hi
+    float *z;         // [B * H][D]
+};
+
+// Wave w owns the output tiles (dv block w / 2 of D / 32, dk blocks
+// NDB / 2 * (w % 2) ..) of KV^T; waves with dv block 0 also sum z.
+template <int D>
+__global__ __launch_bounds__(kLinThreads) void k_lin_reduce(LinArgs a)
+{
+    using G = LGeo<D>;
+    // output tiles per wave: 2 at D = 128; 1 at D = 64 (waves 4-7 only copy)
+    constexpr int NT = G::NDB * G::NDB;
+    constexpr int TPW = NT >= 8 ? NT / 8 : 1;
+    __shared__ __attribute__((aligned(1024))) char sK[2 * G::TILE];
+    __shared__ __attribute__((aligned(1024))) char sV[2 * G::TILE];
+    char LDS_AS *lK = (char LDS_AS *)sK;
+    char LDS_AS *lV = (char LDS_AS *)sV;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hh = lane >> 5;
+    const int bh = blockIdx.x / a.nchunk, chunk = blockIdx.x - bh * a.nchunk;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const __bf16 *Kp = (const __bf16 *)a.k + b * a.sk[0] + h * a.sk[1];
+    const __bf16 *Vp = (const __bf16 *)a.v + b * a.sv[0] + h * a.sv[1];
+    const int N = a.N;
+    const int r0 = chunk * kLinChunk;
+    const int r1 = r0 + kLinChunk < N ? r0 + kLinChunk : N;
+    const int ntiles = (r1 - r0 + kBlock - 1) / kBlock;
+    // tile assignment
+    const int first = wave * TPW;
+    int dvb[TPW], dkb[TPW];
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) {
+        dvb[x] = (first + x) / G::NDB;
+        dkb[x] = (first + x) % G::NDB;
+    }
+    const bool owns = first < NT;               // wave-uniform
+    const bool zwave = owns && (first / G::NDB) == 0;  // this wave's tiles all have dv block 0
+    f32x16 acc[TPW];
+#pragma unroll
+    for (int x = 0; x < TPW; ++x)
+        acc[x] = f32x16{};
+    float zs[TPW] = {};
+
+    lcopy_tile<D>(Kp, a.sk[2], r0, N, lK, wave, lane);
+    lcopy_tile<D>(Vp, a.sv[2], r0, N, lV, wave, lane);
+    for (int u = 0; u < ntiles; ++u) {
+        const int buf = u & 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (u + 1 < ntiles) {
+            lcopy_tile<D>(Kp, a.sk[2], r0 + (u + 1) * kBlock, N, lK + (buf ^ 1) * G::TILE, wave, lane);
+            lcopy_tile<D>(Vp, a.sv[2], r0 + (u + 1) * kBlock, N, lV + (buf ^ 1) * G::TILE, wave, lane);
+        }
+        const char LDS_AS *tK = lK + buf * G::TILE;
+        const char LDS_AS *tV = lV + buf * G::TILE;
+        const int rows_left = N - (r0 + u * kBlock);  // rows past N are repeated copies
+        if (!owns)
+            continue;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            bf16x8 va[TPW], kb[TPW];
+#pragma unroll
+            for (int x = 0; x < TPW; ++x) {
+                va[x] = ltr<D>(tV, lane, t, dvb[x]);
+                kb[x] = relu8(ltr<D>(tK, lane, t, dkb[x]));
+                if (rows_left < kBlock) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (16 * t + 8 * (j >> 2) + 4 * hh + (j & 3) >= rows_left)
+                            kb[x][j] = (__bf16)0.f;
+                }
+            }
+#pragma unroll
+            for (int x = 0; x < TPW; ++x) {
+                acc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x], kb[x], acc[x], 0, 0, 0);
+                if (zwave)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        zs[x] += (float)kb[x][j];
+            }
+        }
+    }
+    // acc[x]: lane holds KV^T[32 dvb + 8 (i / 4) + 4 hh + i % 4][32 dkb + lane % 32]
+    float *out = a.part + (int64_t)blockIdx.x * (D * D + D);
+    if (!owns)
+        return;
+#pragma unroll
+    for (int x = 0; x < TPW; ++x)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int dv = 32 * dvb[x] + 8 * (i >> 2) + 4 * hh + (i & 3);
+            out[dv * D + 32 * dkb[x] + (lane & 31)] = acc[x][i];
+        }
+    if (zwave) {
+#pragma unroll
+        for (int x = 0; x < TPW; ++x) {
+            const float zt = lane_pair_sum(zs[x]);
+            if (hh == 0)
+                out[D * D + 32 * dkb[x] + lane] = zt;
+        }
+    }
+}
+
+// KV^T and z of each (b, h): sum of the chunk partials.
+template <int D>
+__global__ __launch_bounds__(256) void k_lin_combine(LinArgs a)
+{
+    const int bh = blockIdx.y;
+    const int e = blockIdx.x * 256 + threadIdx.x;  // element of D * D + D
+    if (e >= D * D + D)
+        return;
+    float s = 0.f;
+    for (int c = 0; c < a.nchunk; ++c)
+        s += a.part[((int64_t)bh * a.nchunk + c) * (D * D + D) + e];
+    if (e < D * D) {
+        const __bf16 hi = (__bf16)s;
+        a.kv_hi[(int64_t)bh * D * D + e] = hi;
+        a.kv_lo[(int64_t)bh * D * D + e] = (__bf16)(s - (float)hi);
+    } else {
+        a.z[(int64_t)bh * D + (e - D * D)] = s;
+    }
+}
+
+// O^T (D x 32 queries per wave) = KV^T phi(Q)^T with KV^T from LDS (row
+// reads) and phi(Q) as register B operands.
+template <int D>
+__global__ __launch_bounds__(kLinThreads) void k_lin_apply(LinArgs a)
+{
+    using G = LGeo<D>;
+    __shared__ __attribute__((aligned(1024))) char sHi[D * D * 2];
+    __shared__ __attribute__((aligned(1024))) char sLo[D * D * 2];
+    __shared__ float sZ[D];
+    char LDS_AS *lHi = (char LDS_AS *)sHi;
+    char LDS_AS *lLo = (char LDS_AS *)sLo;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int lq = lane & 31, hh = lane >> 5;
+    const int tiles = (a.N + 255) / 256;
+    const int bh = blockIdx.x / tiles, tile = blockIdx.x - bh * tiles;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int N = a.N;
+    // stage KV^T (hi, lo) swizzled like a D-row tile, and z
+    {
+        const __bf16 *hi = a.kv_hi + (int64_t)bh * D * D;
+        const __bf16 *lo = a.kv_lo + (int64_t)bh * D * D;
+        for (int c = threadIdx.x; c < D * G::CPR; c += kLinThreads) {
+            const int row = c / G::CPR, ch = c % G::CPR;
+            const int off = row * G::ROWB + ((ch ^ lswz<D>(row)) << 4);
+            *(bf16x8 LDS_AS *)(lHi + off) = *(const bf16x8 *)(hi + row * D + ch * 8);
+            *(bf16x8 LDS_AS *)(lLo + off) = *(const bf16x8 *)(lo + row * D + ch * 8);
+        }
+        if (threadIdx.x < D)
+            sZ[threadIdx.x] = a.z[(int64_t)bh * D + threadIdx.x];
+    }
+    __syncthreads();
+    const int q = tile * 256 + wave * 32 + lq;
+    const int qr = q < N ? q : N - 1;
+    const __bf16 *Qp = (const __bf16 *)a.q + b * a.sq[0] + h * a.sq[1] + (int64_t)qr * a.sq[2];
+    bf16x8 qf[G::NKS];
+    float den = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < G::NKS; ++ks) {
+        qf[ks] = relu8(*(const bf16x8 *)(Qp + ks * 16 + hh * 8));
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            den = fmaf((float)qf[ks][j], sZ[ks * 16 + hh * 8 + j], den);
+    }
+    den = lane_pair_sum(den);
+    f32x16 o[G::NDB];
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db)
+        o[db] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < G::NKS; ++ks)
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+            const int row = db * 32 + lq;
+            const int off = row * G::ROWB + (((2 * ks + hh) ^ lswz<D>(row)) << 4);
+            const bf16x8 ah = *(const bf16x8 LDS_AS *)(lHi + off);
+            const bf16x8 al = *(const bf16x8 LDS_AS *)(lLo + off);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[ks], o[db], 0, 0, 0);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[ks], o[db], 0, 0, 0);
+        }
+    if (q < N) {
+        const float inv = 1.f / (den + a.eps);
+        __bf16 *orow = (__bf16 *)a.o + b * a.so[0] + h * a.so[1] + (int64_t)q * a.so[2];
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                f32x4 v;
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    v[x] = o[db][4 * i4 + x] * inv;
+                *(bf16x4 *)(orow + db * 32 + 8 * i4 + 4 * hh) = __builtin_convertvector(v, bf16x4);
+            }
+    }
+}
+
+}  // namespace
+
+size_t linear_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D)
+{
+    const int64_t nchunk = (N + kLinChunk - 1) / kLinChunk;
+    const int64_t part = B * H * nchunk * (D * D + D) * 4;
+    const int64_t kv = B * H * D * D * 2 * 2 + B * H * D * 4;
+    return (size_t)(part + kv + 256);
+}
+
+hipError_t launch_linear_attn_bf16(const void *q, const int64_t *sq, const void *k, const int64_t *sk,
+                                   const void *v, const int64_t *sv, void *o, const int64_t *so, int64_t B,
+                                   int64_t H, int64_t N, int64_t D, float eps, void *ws, hipStream_t st)
+{
+    LinArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    for (int i = 0; i < 3; ++i) {
+        a.sq[i] = sq[i];
+        a.sk[i] = sk[i];
+        a.sv[i] = sv[i];
+        a.so[i] = so[i];
+    }
+    a.B = (int32_t)B;
+    a.H = (int32_t)H;
+    a.N = (int32_t)N;
+    a.D = (int32_t)D;
+    a.nchunk = (int32_t)((N + kLinChunk - 1) / kLinChunk);
+    a.eps = eps;
+    char *p = (char *)ws;
+    a.part = (float *)p;
+    p += (size_t)B * H * a.nchunk * (D * D + D) * 4;
+    a.kv_hi = (__bf16 *)p;
+    p += (size_t)B * H * D * D * 2;
+    a.kv_lo = (__bf16 *)p;
+    p += (size_t)B * H * D * D * 2;
+    a.z = (float *)p;
+    const unsigned red = (unsigned)(B * H * a.nchunk);
+    const dim3 comb((unsigned)((D * D + D + 255) / 256), (unsigned)(B * H));
+    const unsigned app = (unsigned)(B * H * ((N + 255) / 256));
+    if (D == 128) {
+        hipLaunchKernelGGL(k_lin_reduce<128>, dim3(red), dim3(kLinThreads), 0, st, a);
+        hipLaunchKernelGGL(k_lin_combine<128>, comb, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_lin_apply<128>, dim3(app), dim3(kLinThreads), 0, st, a);
+    } else {
+        hipLaunchKernelGGL(k_lin_reduce<64>, dim3(red), dim3(kLinThreads), 0, st, a);
+        hipLaunchKernelGGL(k_lin_combine<64>, comb, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_lin_apply<64>, dim3(app), dim3(kLinThreads), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tra

@@ -802,4 +802,55 @@ void tra_kvcache_free(tra_kvcache *c)
     delete c;
 }
 
+
+size_t tra_linear_attn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D)
+{
+    if (B < 0 || H < 0 || N < 0 || (D != 64 && D != 128))
+        return 0;
+    return tra::linear_workspace_bytes(B, H, N, D);
+}
+
+tra_status tra_linear_attn_fwd(const tra_tensor *Q, const tra_tensor *K, const tra_tensor *V, tra_tensor *O,
+                               float eps, void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    const tra_tensor *ts[4] = {Q, K, V, O};
+    for (const tra_tensor *t : ts)
+        if (t == nullptr)
+            return TRA_ERR_INVALID;
+    const bool empty = Q->B == 0 || Q->H == 0 || Q->N == 0;
+    for (const tra_tensor *t : ts) {
+        if (t->B != Q->B || t->H != Q->H || t->N != Q->N || t->D != Q->D)
+            return TRA_ERR_SHAPE;
+        if (t->B < 0 || t->H < 0 || t->N < 0 || t->D < 0)
+            return TRA_ERR_SHAPE;
+    }
+    for (const tra_tensor *t : ts)
+        if (t->dtype != TRA_BF16)
+            return TRA_ERR_UNSUPPORTED;
+    if (Q->D != 64 && Q->D != 128)
+        return TRA_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f))
+        return TRA_ERR_INVALID;
+    for (const tra_tensor *t : ts) {
+        if (t->stride[3] != 1)
+            return TRA_ERR_UNSUPPORTED;
+        for (int j = 0; j < 3; ++j)
+            if (t->stride[j] < 0 || t->stride[j] % 8 != 0)
+                return TRA_ERR_UNSUPPORTED;
+    }
+    if (empty)
+        return TRA_OK;
+    for (const tra_tensor *t : ts)
+        if (t->data == nullptr || ((uintptr_t)t->data) % 16 != 0)
+            return t->data == nullptr ? TRA_ERR_INVALID : TRA_ERR_UNSUPPORTED;
+    if (Q->N >= ((int64_t)1 << 31) || Q->B * Q->H * Q->N >= ((int64_t)1 << 40))
+        return TRA_ERR_UNSUPPORTED;
+    if (workspace == nullptr || workspace_bytes < tra::linear_workspace_bytes(Q->B, Q->H, Q->N, Q->D) ||
+        ((uintptr_t)workspace) % 256 != 0)
+        return TRA_ERR_INVALID;
+    return hip_status(tra::launch_linear_attn_bf16(Q->data, Q->stride, K->data, K->stride, V->data, V->stride,
+                                                   O->data, O->stride, Q->B, Q->H, Q->N, Q->D, eps, workspace,
+                                                   (hipStream_t)hip_stream));
+}
+
 }  // extern "C"

@@ -152,4 +152,10 @@ struct BwdArgs {
 };
 hipError_t launch_attn_bwd_bf16(const BwdArgs &a, hipStream_t st);
 
+// SALAD linear branch (attn_linear_bf16.hip).
+size_t linear_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
+hipError_t launch_linear_attn_bf16(const void *q, const int64_t *sq, const void *k, const int64_t *sk,
+                                   const void *v, const int64_t *sv, void *o, const int64_t *so, int64_t B,
+                                   int64_t H, int64_t N, int64_t D, float eps, void *ws, hipStream_t st);
+
 }  // namespace tra
