@@ -153,6 +153,8 @@ RAGGED = [
     ("radial", 12, 256, "block_eq4", {}, 1, 2, 128, "bf16"),
     ("radial", 9, 256, "block_eq4", dict(sink_frames=1), 1, 2, 64, "bf16"),
     ("radial", 12, 256, "block_eq4", {}, 1, 2, 64, "f32"),
+    ("radial", 6, 70, "element", dict(sink_frames=1), 1, 2, 128, "f32"),
+    ("swa", 4, 100, "element", dict(window=2), 2, 1, 128, "f32"),
 ]
 
 
