@@ -121,23 +121,23 @@ PairSchedule build_pairs(int nqb, int64_t s, const std::vector<int32_t> &row_ptr
 
 void free_mask_buffers(tra_mask *m)
 {
-    hipFree(m->bitmap);
-    hipFree(m->row_ptr);
-    hipFree(m->col_idx);
-    hipFree(m->emask_idx);
-    hipFree(m->emask);
-    hipFree(m->order);
-    hipFree(m->pair_rows);
-    hipFree(m->pair_ptr);
-    hipFree(m->u_col);
-    hipFree(m->u_em);
-    hipFree(m->pair_order);
-    hipFree(m->queue);
-    hipFree(m->t_pair_cols);
-    hipFree(m->t_pair_ptr);
-    hipFree(m->t_u_row);
-    hipFree(m->t_u_em);
-    hipFree(m->t_pair_order);
+    (void)hipFree(m->bitmap);
+    (void)hipFree(m->row_ptr);
+    (void)hipFree(m->col_idx);
+    (void)hipFree(m->emask_idx);
+    (void)hipFree(m->emask);
+    (void)hipFree(m->order);
+    (void)hipFree(m->pair_rows);
+    (void)hipFree(m->pair_ptr);
+    (void)hipFree(m->u_col);
+    (void)hipFree(m->u_em);
+    (void)hipFree(m->pair_order);
+    (void)hipFree(m->queue);
+    (void)hipFree(m->t_pair_cols);
+    (void)hipFree(m->t_pair_ptr);
+    (void)hipFree(m->t_u_row);
+    (void)hipFree(m->t_u_em);
+    (void)hipFree(m->t_pair_order);
 }
 
 bool tensor_ok(const tra_tensor *t) { return t != nullptr && t->data != nullptr; }
@@ -434,27 +434,27 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
         in.bwd_work_items = m->t_npairs;
         in.bwd_tile_loads = m->t_nunion;
     }
-    hipFree(cls);
-    hipFree(cnt);
-    hipFree(row_blocks);
-    hipFree(row_partial);
-    hipFree(row_pred);
-    hipFree(row_eff);
-    hipFree(part_ptr_d);
-    hipFree(part_list);
+    (void)hipFree(cls);
+    (void)hipFree(cnt);
+    (void)hipFree(row_blocks);
+    (void)hipFree(row_partial);
+    (void)hipFree(row_pred);
+    (void)hipFree(row_eff);
+    (void)hipFree(part_ptr_d);
+    (void)hipFree(part_list);
     *out = m;
     return TRA_OK;
 
 fail:
-    hipStreamSynchronize(st);
-    hipFree(cls);
-    hipFree(cnt);
-    hipFree(row_blocks);
-    hipFree(row_partial);
-    hipFree(row_pred);
-    hipFree(row_eff);
-    hipFree(part_ptr_d);
-    hipFree(part_list);
+    (void)hipStreamSynchronize(st);
+    (void)hipFree(cls);
+    (void)hipFree(cnt);
+    (void)hipFree(row_blocks);
+    (void)hipFree(row_partial);
+    (void)hipFree(row_pred);
+    (void)hipFree(row_eff);
+    (void)hipFree(part_ptr_d);
+    (void)hipFree(part_list);
     free_mask_buffers(m);
     delete m;
     return st_;

@@ -111,3 +111,53 @@ def test_oracle_and_product_are_independent():
             assert not imp_prod.search(open(os.path.join(ROOT, "oracle", fn)).read()), fn
     wl = open(os.path.join(ROOT, "workloads", "__init__.py")).read()
     assert not imp_oracle.search(wl) and not imp_prod.search(wl)
+
+
+def _tdesc(B=1, H=1, N=128, D=64, dtype=1, data=0x10000):
+    import static_sparse_spatiotemporal_amd as tra
+    t = tra.TensorDesc()
+    t.data = data
+    t.dtype = dtype
+    t.B, t.H, t.N, t.D = B, H, N, D
+    for i, st in enumerate((H * N * D, N * D, D, 1)):
+        t.stride[i] = st
+    return t
+
+
+def test_bwd_rejects_on_host(lib):
+    t = _tdesc()
+    r = ctypes.byref
+    assert lib.tra_sparse_attn_bwd(None, r(t), r(t), r(t), r(t), None, None, r(t), r(t), r(t), None, 0.0, None) == -1
+    assert lib.tra_sparse_attn_bwd(r(t), r(t), r(t), r(t), r(t), None, None, r(t), r(t), r(t), None, 0.0, None) == -1
+
+
+def test_kvcache_rejects_on_host(lib):
+    out = ctypes.c_void_p(7)
+    assert lib.tra_kvcache_create(1, 1, 128, 64, 4, 1, None) == -1
+    assert lib.tra_kvcache_create(0, 1, 128, 64, 4, 1, ctypes.byref(out)) == -1 and out.value is None
+    assert lib.tra_kvcache_create(1, 1, 128, 64, 0, 1, ctypes.byref(out)) == -1
+    assert lib.tra_kvcache_create(1, 1, 100, 64, 4, 1, ctypes.byref(out)) == -2  # s % 128 != 0
+    assert lib.tra_kvcache_create(1, 1, 128, 96, 4, 1, ctypes.byref(out)) == -2  # D
+    assert lib.tra_kvcache_create(1, 1, 128, 64, 4, 0, ctypes.byref(out)) == -2  # fp32
+    t = _tdesc()
+    assert lib.tra_kvcache_append(None, ctypes.byref(t), ctypes.byref(t), None) == -1
+    assert lib.tra_kvcache_attn(None, ctypes.byref(t), ctypes.byref(t), None, 0.0, None) == -1
+    assert lib.tra_kvcache_get_frames(None, None, None) == -1
+    assert lib.tra_kvcache_reset(None) == -1
+    lib.tra_kvcache_free(None)
+
+
+def test_linear_rejects_on_host(lib):
+    r = ctypes.byref
+    assert lib.tra_linear_attn_workspace_bytes(1, 1, 128, 96) == 0
+    assert lib.tra_linear_attn_workspace_bytes(2, 3, 300, 64) > 0
+    t = _tdesc()
+    f = _tdesc(dtype=0)
+    assert lib.tra_linear_attn_fwd(None, r(t), r(t), r(t), 1e-6, None, 0, None) == -1
+    assert lib.tra_linear_attn_fwd(r(f), r(f), r(f), r(f), 1e-6, None, 0, None) == -2
+    assert lib.tra_linear_attn_fwd(r(t), r(t), r(t), r(t), 1e-6, None, 0, None) == -1      # no workspace
+    assert lib.tra_linear_attn_fwd(r(t), r(t), r(t), r(t), -1.0, None, 0, None) == -1      # eps < 0
+    odd = _tdesc(N=129)
+    assert lib.tra_linear_attn_fwd(r(t), r(odd), r(t), r(t), 1e-6, None, 0, None) == -3   # shapes differ
+    empty = _tdesc(N=0, data=0)
+    assert lib.tra_linear_attn_fwd(r(empty), r(empty), r(empty), r(empty), 1e-6, None, 0, None) == 0
