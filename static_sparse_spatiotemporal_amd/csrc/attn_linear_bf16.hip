@@ -2,16 +2,18 @@
 // linear attention over the same Q, K, V as the sparse branch,
 //   O = phi(Q) (phi(K)^T V) / (phi(Q) . sum_t phi(K_t) + eps),  phi = ReLU,
 // in O(N d^2) per (batch, head).  Three kernels:
-//   k_lin_reduce   one workgroup per (b, h, chunk of 2048 rows): KV^T =
+//   k_lin_reduce   one workgroup per (b, h, chunk of 4096 rows): KV^T =
 //                  V^T phi(K) (d x d, fp32) and z = sum_t phi(K_t) over its
 //                  rows with 32x32x16 bf16 MFMAs; both operands are read
-//                  transposed (ds_read_b64_tr_b16) from double-buffered
-//                  K/V tiles;
+//                  transposed (ds_read_b64_tr_b16) from a four-stage LDS
+//                  ring of 64-row K/V tiles (three tiles in flight);
 //   k_lin_combine  sums the chunks, stores KV^T as a bf16 pair (hi + lo,
 //                  about 16 significant bits) and z in fp32;
-//   k_lin_apply    one workgroup per 256 queries: O^T = KV^T phi(Q)^T with
-//                  phi(Q) as the register B operand (two MFMAs per step for
-//                  hi and lo), the denominator phi(Q) . z per lane.
+//   k_lin_apply    one workgroup per 1024 queries (four tiles of 256, the
+//                  next tile's Q loaded while the current one is used):
+//                  O^T = KV^T phi(Q)^T with phi(Q) as the register B operand
+//                  (two MFMAs per step for hi and lo), the denominator
+//                  phi(Q) . z per lane.
 // The path is HBM-bound (Q, K, V read once, O written once).
 #include "attn_common.h"
 
@@ -21,15 +23,19 @@ namespace {
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kLinThreads = 512;  // 8 waves
-constexpr int kLinChunk = 2048;   // rows per reduce workgroup
+constexpr int kLinChunk = 4096;   // rows per reduce workgroup
+constexpr int kApplyRows = 1024;  // queries per apply workgroup (4 tiles of 256)
+
+constexpr int kLinRows = 64;     // rows per K/V tile of the reduce kernel
+constexpr int kLinStages = 4;    // tiles in the LDS ring (three in flight)
 
 template <int D>
 struct LGeo {
     static constexpr int ROWB = D * 2;
-    static constexpr int TILE = kBlock * ROWB;
+    static constexpr int TILE = kLinRows * ROWB;                 // one K or V tile
     static constexpr int CPR = D / 8;
     static constexpr int RPI = 64 / CPR;
-    static constexpr int NCOPY = kBlock * CPR / kLinThreads;
+    static constexpr int NCOPY = kLinRows * CPR / kLinThreads;   // copies per thread per tile
     static constexpr int NKS = D / 16;
     static constexpr int NDB = D / 32;
 };
@@ -40,7 +46,7 @@ __device__ inline int lswz(int row)
     return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
 
-// Copy a 128-row tile (rows row0 .., clamped to N - 1) of X into LDS.
+// Copy a kLinRows-row tile (rows row0 .., clamped to N - 1) of X into LDS.
 template <int D>
 __device__ inline void lcopy_tile(const __bf16 *X, int64_t stride, int row0, int N, char LDS_AS *dst, int wave,
                                   int lane)
@@ -56,6 +62,12 @@ __device__ inline void lcopy_tile(const __bf16 *X, int64_t stride, int row0, int
                                          (void LDS_AS *)(dst + (8 * i + wave) * 1024), 16, 0, 0);
     }
 }
+
+// s_waitcnt immediate: vmcnt n (0 .. 63, split over bits 3:0 and 15:14),
+// lgkmcnt 0, expcnt untouched.  The builtin form lets the compiler account
+// for the wait, so it adds no drain of its own before reads of an LDS stage
+// that is already complete.
+constexpr int vm_lgkm_wait(int n) { return ((n >> 4) << 14) | 0x70 | (n & 15); }
 
 // Transposed operand: 32 columns (block cb) x 16 rows 16 t + {8 (j / 4) +
 // 4 (lane / 32) + j % 4}, j = 0 .. 7.
@@ -108,10 +120,14 @@ __global__ __launch_bounds__(kLinThreads) void k_lin_reduce(LinArgs a)
     // output tiles per wave: 2 at D = 128; 1 at D = 64 (waves 4-7 only copy)
     constexpr int NT = G::NDB * G::NDB;
     constexpr int TPW = NT >= 8 ? NT / 8 : 1;
-    __shared__ __attribute__((aligned(1024))) char sK[2 * G::TILE];
-    __shared__ __attribute__((aligned(1024))) char sV[2 * G::TILE];
-    char LDS_AS *lK = (char LDS_AS *)sK;
-    char LDS_AS *lV = (char LDS_AS *)sV;
+    // ring stages (K tile, then V tile); one variable per stage so the
+    // compiler tells copies into one stage from reads of another
+    __shared__ __attribute__((aligned(1024))) char sT0[2 * G::TILE];
+    __shared__ __attribute__((aligned(1024))) char sT1[2 * G::TILE];
+    __shared__ __attribute__((aligned(1024))) char sT2[2 * G::TILE];
+    __shared__ __attribute__((aligned(1024))) char sT3[2 * G::TILE];
+    __shared__ __attribute__((aligned(1024))) char sT4[kLinStages > 4 ? 2 * G::TILE : 1024];
+    static_assert(kLinStages == 4 || kLinStages == 5, "four or five ring stages");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hh = lane >> 5;
@@ -122,7 +138,7 @@ __global__ __launch_bounds__(kLinThreads) void k_lin_reduce(LinArgs a)
     const int N = a.N;
     const int r0 = chunk * kLinChunk;
     const int r1 = r0 + kLinChunk < N ? r0 + kLinChunk : N;
-    const int ntiles = (r1 - r0 + kBlock - 1) / kBlock;
+    const int ntiles = (r1 - r0 + kLinRows - 1) / kLinRows;
     // tile assignment
     const int first = wave * TPW;
     int dvb[TPW], dkb[TPW];
@@ -139,45 +155,69 @@ __global__ __launch_bounds__(kLinThreads) void k_lin_reduce(LinArgs a)
         acc[x] = f32x16{};
     float zs[TPW] = {};
 
-    lcopy_tile<D>(Kp, a.sk[2], r0, N, lK, wave, lane);
-    lcopy_tile<D>(Vp, a.sv[2], r0, N, lV, wave, lane);
-    for (int u = 0; u < ntiles; ++u) {
-        const int buf = u & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (u + 1 < ntiles) {
-            lcopy_tile<D>(Kp, a.sk[2], r0 + (u + 1) * kBlock, N, lK + (buf ^ 1) * G::TILE, wave, lane);
-            lcopy_tile<D>(Vp, a.sv[2], r0 + (u + 1) * kBlock, N, lV + (buf ^ 1) * G::TILE, wave, lane);
-        }
-        const char LDS_AS *tK = lK + buf * G::TILE;
-        const char LDS_AS *tV = lV + buf * G::TILE;
-        const int rows_left = N - (r0 + u * kBlock);  // rows past N are repeated copies
-        if (!owns)
-            continue;
+    // stage S of the ring (S is a constant once the step loop is unrolled)
+#define LIN_STAGE(S)                                                                                      \
+    ((S) % kLinStages == 0   ? (char LDS_AS *)sT0                                                         \
+     : (S) % kLinStages == 1 ? (char LDS_AS *)sT1                                                         \
+     : (S) % kLinStages == 2 ? (char LDS_AS *)sT2                                                         \
+     : (S) % kLinStages == 3 ? (char LDS_AS *)sT3                                                         \
+                             : (char LDS_AS *)sT4)
+    // tiles past the last one re-read the last tile (from L2) so that every
+    // step issues the same copies and waits
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            bf16x8 va[TPW], kb[TPW];
+    for (int p = 0; p < kLinStages - 1; ++p) {
+        const int t = p < ntiles ? p : ntiles - 1;
+        lcopy_tile<D>(Kp, a.sk[2], r0 + t * kLinRows, N, LIN_STAGE(p), wave, lane);
+        lcopy_tile<D>(Vp, a.sv[2], r0 + t * kLinRows, N, LIN_STAGE(p) + G::TILE, wave, lane);
+    }
+    for (int u0 = 0; u0 < ntiles; u0 += kLinStages) {
+        // Step u: tile u is in stage u % L, tiles u + 1 .. u + L - 2 are in
+        // flight; after the barrier no wave still reads stage (u - 1) % L
+        // (tile u - 1), which receives tile u + L - 1.
 #pragma unroll
-            for (int x = 0; x < TPW; ++x) {
-                va[x] = ltr<D>(tV, lane, t, dvb[x]);
-                kb[x] = relu8(ltr<D>(tK, lane, t, dkb[x]));
-                if (rows_left < kBlock) {
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        if (16 * t + 8 * (j >> 2) + 4 * hh + (j & 3) >= rows_left)
-                            kb[x][j] = (__bf16)0.f;
-                }
+        for (int S = 0; S < kLinStages; ++S) {
+            const int u = u0 + S;
+            __builtin_amdgcn_s_waitcnt(vm_lgkm_wait((kLinStages - 2) * 2 * G::NCOPY));
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");  // no LDS access moves across the barrier
+            {
+                const int t = u + kLinStages - 1 < ntiles ? u + kLinStages - 1 : ntiles - 1;
+                char LDS_AS *dst = LIN_STAGE(S + kLinStages - 1);
+                lcopy_tile<D>(Kp, a.sk[2], r0 + t * kLinRows, N, dst, wave, lane);
+                lcopy_tile<D>(Vp, a.sv[2], r0 + t * kLinRows, N, dst + G::TILE, wave, lane);
             }
+            if (!owns || u >= ntiles)
+                continue;
+            const char LDS_AS *tK = LIN_STAGE(S);
+            const char LDS_AS *tV = tK + G::TILE;
+            const int rows_left = N - (r0 + u * kLinRows);  // rows past N are repeated copies
 #pragma unroll
-            for (int x = 0; x < TPW; ++x) {
-                acc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x], kb[x], acc[x], 0, 0, 0);
-                if (zwave)
+            for (int t = 0; t < kLinRows / 16; ++t) {
+                bf16x8 va[TPW], kb[TPW];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        zs[x] += (float)kb[x][j];
+                for (int x = 0; x < TPW; ++x) {
+                    va[x] = ltr<D>(tV, lane, t, dvb[x]);
+                    kb[x] = relu8(ltr<D>(tK, lane, t, dkb[x]));
+                    if (rows_left < kLinRows) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            if (16 * t + 8 * (j >> 2) + 4 * hh + (j & 3) >= rows_left)
+                                kb[x][j] = (__bf16)0.f;
+                    }
+                }
+#pragma unroll
+                for (int x = 0; x < TPW; ++x) {
+                    acc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x], kb[x], acc[x], 0, 0, 0);
+                    if (zwave)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            zs[x] += (float)kb[x][j];
+                }
             }
         }
     }
+#undef LIN_STAGE
+    __builtin_amdgcn_s_waitcnt(0);  // no copy may land after the workgroup ends
     // acc[x]: lane holds KV^T[32 dvb + 8 (i / 4) + 4 hh + i % 4][32 dkb + lane % 32]
     float *out = a.part + (int64_t)blockIdx.x * (D * D + D);
     if (!owns)
@@ -228,13 +268,16 @@ __global__ __launch_bounds__(kLinThreads) void k_lin_apply(LinArgs a)
     __shared__ __attribute__((aligned(1024))) char sHi[D * D * 2];
     __shared__ __attribute__((aligned(1024))) char sLo[D * D * 2];
     __shared__ float sZ[D];
+    // per wave: its 32 x D output tile, staged for row-contiguous stores
+    __shared__ __attribute__((aligned(1024))) char sO[(kLinThreads / 64) * 32 * D * 2];
     char LDS_AS *lHi = (char LDS_AS *)sHi;
     char LDS_AS *lLo = (char LDS_AS *)sLo;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    char LDS_AS *lO = (char LDS_AS *)sO + wave * 32 * G::ROWB;
     const int lq = lane & 31, hh = lane >> 5;
-    const int tiles = (a.N + 255) / 256;
-    const int bh = blockIdx.x / tiles, tile = blockIdx.x - bh * tiles;
+    const int groups = (a.N + kApplyRows - 1) / kApplyRows;
+    const int bh = blockIdx.x / groups, grp = blockIdx.x - bh * groups;
     const int b = bh / a.H, h = bh - b * a.H;
     const int N = a.N;
     // stage KV^T (hi, lo) swizzled like a D-row tile, and z
@@ -251,47 +294,89 @@ __global__ __launch_bounds__(kLinThreads) void k_lin_apply(LinArgs a)
             sZ[threadIdx.x] = a.z[(int64_t)bh * D + threadIdx.x];
     }
     __syncthreads();
-    const int q = tile * 256 + wave * 32 + lq;
-    const int qr = q < N ? q : N - 1;
-    const __bf16 *Qp = (const __bf16 *)a.q + b * a.sq[0] + h * a.sq[1] + (int64_t)qr * a.sq[2];
-    bf16x8 qf[G::NKS];
-    float den = 0.f;
+    const int tiles = (N + 255) / 256;
+    const int tbeg = grp * (kApplyRows / 256);
+    const int tend = tbeg + kApplyRows / 256 < tiles ? tbeg + kApplyRows / 256 : tiles;
+    const __bf16 *Qbh = (const __bf16 *)a.q + b * a.sq[0] + h * a.sq[1];
+    // raw Q of this lane's query in the current tile; the next tile's rows
+    // are loaded while the current one is multiplied
+    // (the tile loop is unrolled so that the loaded registers need no
+    // copies between iterations)
+    bf16x8 qraw[G::NKS];
+    auto load_q = [&](int tile) {
+        const int q = tile * 256 + wave * 32 + lq;
+        const __bf16 *Qp = Qbh + (int64_t)(q < N ? q : N - 1) * a.sq[2];
 #pragma unroll
-    for (int ks = 0; ks < G::NKS; ++ks) {
-        qf[ks] = relu8(*(const bf16x8 *)(Qp + ks * 16 + hh * 8));
+        for (int ks = 0; ks < G::NKS; ++ks)
+            qraw[ks] = *(const bf16x8 *)(Qp + ks * 16 + hh * 8);
+    };
+    load_q(tbeg);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            den = fmaf((float)qf[ks][j], sZ[ks * 16 + hh * 8 + j], den);
-    }
-    den = lane_pair_sum(den);
-    f32x16 o[G::NDB];
+    for (int i = 0; i < kApplyRows / 256; ++i) {
+        const int tile = tbeg + i;
+        if (tile >= tend)
+            break;
+        const int q = tile * 256 + wave * 32 + lq;
+        bf16x8 qf[G::NKS];
 #pragma unroll
-    for (int db = 0; db < G::NDB; ++db)
-        o[db] = f32x16{};
+        for (int ks = 0; ks < G::NKS; ++ks)
+            qf[ks] = relu8(qraw[ks]);
+        if (i + 1 < kApplyRows / 256 && tile + 1 < tend)
+            load_q(tile + 1);
+        float den = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < G::NKS; ++ks)
+        for (int ks = 0; ks < G::NKS; ++ks)
 #pragma unroll
-        for (int db = 0; db < G::NDB; ++db) {
-            const int row = db * 32 + lq;
-            const int off = row * G::ROWB + (((2 * ks + hh) ^ lswz<D>(row)) << 4);
-            const bf16x8 ah = *(const bf16x8 LDS_AS *)(lHi + off);
-            const bf16x8 al = *(const bf16x8 LDS_AS *)(lLo + off);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[ks], o[db], 0, 0, 0);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[ks], o[db], 0, 0, 0);
-        }
-    if (q < N) {
-        const float inv = 1.f / (den + a.eps);
-        __bf16 *orow = (__bf16 *)a.o + b * a.so[0] + h * a.so[1] + (int64_t)q * a.so[2];
+            for (int j = 0; j < 8; ++j)
+                den = fmaf((float)qf[ks][j], sZ[ks * 16 + hh * 8 + j], den);
+        den = lane_pair_sum(den);
+        f32x16 o[G::NDB];
 #pragma unroll
         for (int db = 0; db < G::NDB; ++db)
+            o[db] = f32x16{};
+        // KV^T is re-read from LDS per tile: an opaque zero keeps the reads
+        // (D * D * 4 bytes per lane) from being hoisted out of the tile loop
+        int rebase = 0;
+        asm volatile("" : "+v"(rebase));
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                f32x4 v;
+        for (int ks = 0; ks < G::NKS; ++ks)
 #pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    v[x] = o[db][4 * i4 + x] * inv;
-                *(bf16x4 *)(orow + db * 32 + 8 * i4 + 4 * hh) = __builtin_convertvector(v, bf16x4);
+            for (int db = 0; db < G::NDB; ++db) {
+                const int row = db * 32 + lq;
+                const int off = rebase + row * G::ROWB + (((2 * ks + hh) ^ lswz<D>(row)) << 4);
+                const bf16x8 ah = *(const bf16x8 LDS_AS *)(lHi + off);
+                const bf16x8 al = *(const bf16x8 LDS_AS *)(lLo + off);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[ks], o[db], 0, 0, 0);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[ks], o[db], 0, 0, 0);
             }
+        // O^T tile -> LDS rows (16-byte chunks XOR-swizzled by row), then
+        // 16 bytes per lane, 64 / CPR rows per store.  Lanes past N computed
+        // row N - 1 from the same inputs and store the same bits there; the
+        // unconditional stores keep the wait for the next tile's Q at the
+        // stores issued after it.
+        {
+            const float inv = 1.f / (den + a.eps);
+#pragma unroll
+            for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    f32x4 v;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        v[x] = o[db][4 * i4 + x] * inv;
+                    const int ch = (4 * db + i4) ^ (lq & (G::CPR - 1));
+                    *(bf16x4 LDS_AS *)(lO + lq * G::ROWB + ch * 16 + hh * 8) = __builtin_convertvector(v, bf16x4);
+                }
+            const int rsub = lane / G::CPR, ch = lane % G::CPR;
+#pragma unroll
+            for (int i = 0; i < 32 / G::RPI; ++i) {
+                const int r = i * G::RPI + rsub;
+                const bf16x8 val = *(const bf16x8 LDS_AS *)(lO + r * G::ROWB + ((ch ^ (r & (G::CPR - 1))) << 4));
+                const int qo = tile * 256 + wave * 32 + r;
+                __bf16 *orow = (__bf16 *)a.o + b * a.so[0] + h * a.so[1] + (int64_t)(qo < N ? qo : N - 1) * a.so[2];
+                *(bf16x8 *)(orow + ch * 8) = val;
+            }
+        }
     }
 }
 
@@ -336,7 +421,7 @@ hipError_t launch_linear_attn_bf16(const void *q, const int64_t *sq, const void 
     a.z = (float *)p;
     const unsigned red = (unsigned)(B * H * a.nchunk);
     const dim3 comb((unsigned)((D * D + D + 255) / 256), (unsigned)(B * H));
-    const unsigned app = (unsigned)(B * H * ((N + 255) / 256));
+    const unsigned app = (unsigned)(B * H * ((N + kApplyRows - 1) / kApplyRows));
     if (D == 128) {
         hipLaunchKernelGGL(k_lin_reduce<128>, dim3(red), dim3(kLinThreads), 0, st, a);
         hipLaunchKernelGGL(k_lin_combine<128>, comb, dim3(256), 0, st, a);

@@ -36,7 +36,8 @@ def check(tra, B, H, n, D, seed, rows=None, scale=1.0):
     assert err <= 2e-2 and rel <= 1e-2
 
 
-@pytest.mark.parametrize("n,D", [(300, 64), (300, 128), (128, 128), (2048, 64), (2100, 128)])
+@pytest.mark.parametrize("n,D", [(1, 64), (300, 64), (300, 128), (128, 128), (2048, 64), (2100, 128),
+                                 (4100, 128), (5000, 64)])
 def test_linear_full_parity(tra, n, D):
     check(tra, 2, 2, n, D, seed=900 + n + D)
 
