@@ -88,6 +88,13 @@ def _load():
             ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int]
+        lib.orc_salad_gate.argtypes = [
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int]
+        lib.orc_salad_output_rows.argtypes = [
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int]
         lib.orc_row_counts.argtypes = [P(_Mask), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_void_p]
         lib.orc_attention_rows.argtypes = [
@@ -325,3 +332,55 @@ def linear_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows: np.
                                       float(eps), rows.ctypes.data, rows.shape[0], o.ctypes.data,
                                       threads or default_threads())
     return o
+
+
+def _dtype_code(*arrs) -> int:
+    if all(a.dtype == np.float32 for a in arrs):
+        return F32
+    if all(a.dtype == np.uint16 for a in arrs):
+        return BF16
+    raise TypeError("arrays must all be float32 or all uint16 (bfloat16 bits)")
+
+
+def salad_gate(x: np.ndarray, w: np.ndarray, bias: float = 0.0, threads: int | None = None) -> np.ndarray:
+    """fp64 SALAD gate: g[b] = mean_n sigmoid(x[b, n, :] . w + bias).
+
+    x: [B, N, C], w: [C], both float32 or both uint16 bfloat16 bits.
+    Returns g [B] float64.
+    """
+    B, N, C = x.shape
+    assert w.shape == (C,)
+    dtype = _dtype_code(x, w)
+    x, w = np.ascontiguousarray(x), np.ascontiguousarray(w)
+    g = np.zeros(B, dtype=np.float64)
+    _load().orc_salad_gate(dtype, x.ctypes.data, w.ctypes.data, float(bias), B, N, C, g.ctypes.data,
+                           threads or default_threads())
+    return g
+
+
+def salad_output_rows(o_sparse: np.ndarray, o_lin: np.ndarray, w: np.ndarray, bias, g: np.ndarray,
+                      rows: np.ndarray | None = None, threads: int | None = None) -> np.ndarray:
+    """fp64 SALAD output rows: O_s + g[b] * (O_l W^T + bias) in the merged-head
+    channel space (channel h * d + e of token n is [b, h, n, e]).
+
+    o_sparse, o_lin: [B, H, N, d]; w: [H*d, H*d] (same dtype: float32 or
+    uint16 bfloat16 bits); bias: None or [H*d] float; g: [B] float.
+    rows: (b, n) pairs, default all.  Returns [nrows, H*d] float64.
+    """
+    B, H, N, d = o_sparse.shape
+    C = H * d
+    assert o_lin.shape == o_sparse.shape and w.shape == (C, C)
+    dtype = _dtype_code(o_sparse, o_lin, w)
+    o_sparse, o_lin, w = (np.ascontiguousarray(a) for a in (o_sparse, o_lin, w))
+    bias_arr = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64).reshape(C)
+    g = np.ascontiguousarray(g, dtype=np.float64).reshape(B)
+    if rows is None:
+        bb, nn = np.meshgrid(np.arange(B), np.arange(N), indexing="ij")
+        rows = np.stack([bb.ravel(), nn.ravel()], axis=1)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 2)
+    out = np.zeros((rows.shape[0], C), dtype=np.float64)
+    _load().orc_salad_output_rows(dtype, o_sparse.ctypes.data, o_lin.ctypes.data, w.ctypes.data,
+                                  None if bias_arr is None else bias_arr.ctypes.data, g.ctypes.data,
+                                  B, H, N, d, rows.ctypes.data, rows.shape[0], out.ctypes.data,
+                                  threads or default_threads())
+    return out

@@ -696,3 +696,126 @@ void orc_linear_attention_rows(int dtype, const void *q, const void *k, const vo
     free(jobs);
     free(tid);
 }
+
+/* ---- SALAD gate and output ------------------------------------------------ */
+
+typedef struct {
+    int dtype;
+    const void *x, *w;
+    double bias;
+    int64_t N, C;
+    int64_t begin, end; /* samples b */
+    double *g_out;
+} gate_job;
+
+static void *gate_worker(void *arg)
+{
+    gate_job *j = (gate_job *)arg;
+    for (int64_t b = j->begin; b < j->end; b++) {
+        double sum = 0.0;
+        for (int64_t n = 0; n < j->N; n++) {
+            double z = j->bias;
+            for (int64_t c = 0; c < j->C; c++)
+                z += load_value(j->dtype, j->x, (b * j->N + n) * j->C + c) * load_value(j->dtype, j->w, c);
+            sum += 1.0 / (1.0 + exp(-z));
+        }
+        j->g_out[b] = sum / (double)j->N;
+    }
+    return NULL;
+}
+
+void orc_salad_gate(int dtype, const void *x, const void *w, double bias, int64_t B, int64_t N, int64_t C,
+                    double *g_out, int threads)
+{
+    if (threads < 1)
+        threads = 1;
+    if (threads > B)
+        threads = B > 0 ? (int)B : 1;
+    gate_job *jobs = (gate_job *)calloc((size_t)threads, sizeof(gate_job));
+    pthread_t *tid = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    for (int t = 0; t < threads; t++) {
+        gate_job *j = &jobs[t];
+        j->dtype = dtype;
+        j->x = x;
+        j->w = w;
+        j->bias = bias;
+        j->N = N;
+        j->C = C;
+        j->begin = B * t / threads;
+        j->end = B * (t + 1) / threads;
+        j->g_out = g_out;
+        pthread_create(&tid[t], NULL, gate_worker, j);
+    }
+    for (int t = 0; t < threads; t++)
+        pthread_join(tid[t], NULL);
+    free(jobs);
+    free(tid);
+}
+
+typedef struct {
+    int dtype;
+    const void *os, *ol, *w;
+    const double *bias, *g;
+    int64_t H, N, d;
+    const int64_t *rows;
+    int64_t begin, end;
+    double *out;
+} sout_job;
+
+static void *sout_worker(void *arg)
+{
+    sout_job *j = (sout_job *)arg;
+    const int64_t H = j->H, N = j->N, d = j->d, C = H * d;
+    double *in = (double *)malloc((size_t)C * sizeof(double));
+    for (int64_t r = j->begin; r < j->end; r++) {
+        const int64_t b = j->rows[2 * r], n = j->rows[2 * r + 1];
+        /* channel c of token n: head c / d, element c % d */
+        for (int64_t c = 0; c < C; c++)
+            in[c] = load_value(j->dtype, j->ol, ((b * H + c / d) * N + n) * d + c % d);
+        for (int64_t co = 0; co < C; co++) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < C; c++)
+                acc += in[c] * load_value(j->dtype, j->w, co * C + c);
+            if (j->bias)
+                acc += j->bias[co];
+            j->out[r * C + co] =
+                load_value(j->dtype, j->os, ((b * H + co / d) * N + n) * d + co % d) + j->g[b] * acc;
+        }
+    }
+    free(in);
+    return NULL;
+}
+
+void orc_salad_output_rows(int dtype, const void *o_sparse, const void *o_lin, const void *w, const double *bias,
+                           const double *g, int64_t B, int64_t H, int64_t N, int64_t d, const int64_t *rows,
+                           int64_t nrows, double *out, int threads)
+{
+    (void)B;
+    if (threads < 1)
+        threads = 1;
+    if (threads > nrows)
+        threads = nrows > 0 ? (int)nrows : 1;
+    sout_job *jobs = (sout_job *)calloc((size_t)threads, sizeof(sout_job));
+    pthread_t *tid = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    for (int t = 0; t < threads; t++) {
+        sout_job *j = &jobs[t];
+        j->dtype = dtype;
+        j->os = o_sparse;
+        j->ol = o_lin;
+        j->w = w;
+        j->bias = bias;
+        j->g = g;
+        j->H = H;
+        j->N = N;
+        j->d = d;
+        j->rows = rows;
+        j->begin = nrows * t / threads;
+        j->end = nrows * (t + 1) / threads;
+        j->out = out;
+        pthread_create(&tid[t], NULL, sout_worker, j);
+    }
+    for (int t = 0; t < threads; t++)
+        pthread_join(tid[t], NULL);
+    free(jobs);
+    free(tid);
+}

@@ -27,6 +27,10 @@
  *   - Radial Attention, section 4 (complexity): the central-band term counts
  *     a "sink" beside the band.  sink_frames > 0 adds it in its plainest
  *     form: every query keeps every key of the first sink_frames frames.
+ *   - SALAD, sections 2.1-2.2: the ReLU-kernel linear-attention branch over
+ *     the same Q, K, V, its scalar gate (mean over tokens of a sigmoid of a
+ *     linear map of the block input) and the gated, projected sum with the
+ *     sparse branch.
  *
  * All mask arithmetic is integer.  Attention is fp64 over the exact input
  * values (bf16 or fp32, widened exactly).
@@ -143,6 +147,28 @@ void orc_attention_bwd_rows(int dtype, const void *q, const void *k, const void 
 void orc_linear_attention_rows(int dtype, const void *q, const void *k, const void *v, int64_t B, int64_t H,
                                int64_t n, int64_t d, double eps, const int64_t *rows, int64_t nrows,
                                double *o_out, int threads);
+
+/* SALAD gate (page "SALAD", section 2.2): a learned linear map of the block
+ * input to one value per token, a sigmoid, then the mean over the sequence,
+ * one scalar per sample:
+ *   g[b] = (1 / N) sum_n sigmoid(x[b, n, :] . w + bias),
+ *   sigmoid(z) = 1 / (1 + exp(-z)).
+ *   x : [B, N, C] contiguous (dtype), w : [C] (dtype), g_out : B doubles. */
+void orc_salad_gate(int dtype, const void *x, const void *w, double bias, int64_t B, int64_t N, int64_t C,
+                    double *g_out, int threads);
+
+/* SALAD output (page "SALAD", sections 2.1-2.2): the sparse branch plus the
+ * gated projection of the linear branch, in the merged-head channel space
+ * c = h * d + e (C = H * d channels):
+ *   out[b, n, c'] = O_s[b, n, c'] + g[b] * (sum_c O_l[b, n, c] W[c', c] + bias[c'])
+ * O_s, O_l : [B, H, N, d] contiguous (dtype), so channel c of token n is
+ *            element [b, c / d, n, c % d];
+ * W        : [C, C] row-major (dtype), the projection (out = in W^T);
+ * bias     : C doubles, or NULL for none;  g : B doubles;
+ * rows     : nrows pairs (b, n);  out : nrows x C. */
+void orc_salad_output_rows(int dtype, const void *o_sparse, const void *o_lin, const void *w, const double *bias,
+                           const double *g, int64_t B, int64_t H, int64_t N, int64_t d, const int64_t *rows,
+                           int64_t nrows, double *out, int threads);
 
 #ifdef __cplusplus
 }
