@@ -105,11 +105,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void attn_fwd_bf16(AttnArgs a)
 {
     using G = Geo<D>;
-    __shared__ __attribute__((aligned(1024))) char sK[2 * G::TILE];
-    __shared__ __attribute__((aligned(1024))) char sV[2 * G::TILE];
+    // Double buffers, one LDS array each: with the buffer named statically
+    // in every tile step, the compiler can tell the copy into one buffer
+    // from the operand reads of the other and does not wait for the next
+    // tile's copy before reading the current one.
+    __shared__ __attribute__((aligned(1024))) char sK0[G::TILE];
+    __shared__ __attribute__((aligned(1024))) char sK1[G::TILE];
+    __shared__ __attribute__((aligned(1024))) char sV0[G::TILE];
+    __shared__ __attribute__((aligned(1024))) char sV1[G::TILE];
     __shared__ int sItem;
-    char LDS_AS *lK = (char LDS_AS *)sK;
-    char LDS_AS *lV = (char LDS_AS *)sV;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -163,8 +167,8 @@ void attn_fwd_bf16(AttnArgs a)
 
         auto kcol = [&](int u) { return STREAM ? u : u_col[u]; };
         if (u0 < u1) {
-            copy_tile<D>(Kp, a.sk[2], kcol(u0) * kBlock, a.Nk, lK, wave, crow0, colK, offK);
-            copy_tile<D>(Vp, a.sv[2], kcol(u0) * kBlock, a.Nk, lV, wave, crow0, colV, offV);
+            copy_tile<D>(Kp, a.sk[2], kcol(u0) * kBlock, a.Nk, (char LDS_AS *)sK0, wave, crow0, colK, offK);
+            copy_tile<D>(Vp, a.sv[2], kcol(u0) * kBlock, a.Nk, (char LDS_AS *)sV0, wave, crow0, colV, offV);
         }
         bf16x8 qf[G::NKS];
         if (active) {
@@ -179,22 +183,39 @@ void attn_fwd_bf16(AttnArgs a)
             o[db] = f32x16{};
         float m = kNegInf, l = 0.f;
 
-        for (int u = u0; u < u1; ++u) {
-            const int buf = (u - u0) & 1;
+        // Tile u is in buffer (u - u0) & 1; the loop takes two tiles per
+        // trip so that the buffer of each step is a constant.
+        for (int u2 = u0; u2 < u1; u2 += 2)
+#pragma unroll
+        for (int buf = 0; buf < 2; ++buf) {
+            const int u = u2 + buf;
+            if (u >= u1)
+                break;
+            // The element mask word of a partly kept tile is loaded under the
+            // wait for tile u, never after the next tile's copies.
+            const int em = active ? (STREAM ? -1 : u_em[2 * u + half]) : kAbsent;
+            uint4 mw = {0u, 0u, 0u, 0u};
+            if (em >= 0)
+                mw = ((const uint4 *)a.mask.emask)[(size_t)em * kBlock + w4 * 32 + lq];
             // Tile u has landed everywhere and every wave is done with tile
             // u - 1, whose buffer now receives tile u + 1.
             wait_copies();
             __syncthreads();
-            if (u + 1 < u1) {
-                const int nb = buf ^ 1;
-                copy_tile<D>(Kp, a.sk[2], kcol(u + 1) * kBlock, a.Nk, lK + nb * G::TILE, wave, crow0, colK, offK);
-                copy_tile<D>(Vp, a.sv[2], kcol(u + 1) * kBlock, a.Nk, lV + nb * G::TILE, wave, crow0, colV, offV);
+            // Every step issues the same copies (the last one of the item
+            // re-copies tile u into the free buffer), so the outstanding
+            // count at each wait is the same on every path and the
+            // compiler's waits stay exact.
+            {
+                const int un = u + 1 < u1 ? u + 1 : u;
+                char LDS_AS *nK = (char LDS_AS *)(buf == 0 ? sK1 : sK0);
+                char LDS_AS *nV = (char LDS_AS *)(buf == 0 ? sV1 : sV0);
+                copy_tile<D>(Kp, a.sk[2], kcol(un) * kBlock, a.Nk, nK, wave, crow0, colK, offK);
+                copy_tile<D>(Vp, a.sv[2], kcol(un) * kBlock, a.Nk, nV, wave, crow0, colV, offV);
             }
-            const int em = active ? (STREAM ? -1 : u_em[2 * u + half]) : kAbsent;
             if (em == kAbsent)
                 continue;
-            const char LDS_AS *tK = lK + buf * G::TILE;
-            const char LDS_AS *tV = lV + buf * G::TILE;
+            const char LDS_AS *tK = (const char LDS_AS *)(buf == 0 ? sK0 : sK1);
+            const char LDS_AS *tV = (const char LDS_AS *)(buf == 0 ? sV0 : sV1);
 
             // ---- S^T = K Q^T: 128 keys x 32 queries ----
             f32x16 s[4];
@@ -221,7 +242,6 @@ void attn_fwd_bf16(AttnArgs a)
 
             // ---- element mask of a partly kept tile ----
             if (em >= 0) {
-                const uint4 mw = ((const uint4 *)a.mask.emask)[(size_t)em * kBlock + w4 * 32 + lq];
                 const uint32_t words[4] = {mw.x, mw.y, mw.z, mw.w};
 #pragma unroll
                 for (int kb4 = 0; kb4 < 4; ++kb4)
@@ -345,11 +365,16 @@ void attn_fwd_bf16(AttnArgs a)
         const int u0 = split * a.split_tiles;
         const int u1 = u0 + a.split_tiles < a.nkv_tiles ? u0 + a.split_tiles : a.nkv_tiles;
         item(bh, row, u0, u1, split);
+        wait_copies();  // the last step's copy must land before the workgroup ends
     } else {
         WorkQueue wq(a.mask.queue, a.mask.pair_order, a.mask.npairs, kPairChunk, a.B * a.H);
         int wx = xcd_id(), wtries = 0, bh = 0, pair = 0;
         while (wq.next(wx, wtries, &sItem, bh, pair))
             item(bh, pair_rows[2 * pair + half], pair_ptr[pair], pair_ptr[pair + 1], 0);
+        // The last step of an item re-copies its tile into the free buffer.
+        // A wave's copies land in issue order, so the next item's first copy
+        // still wins; only the workgroup's end has to wait for the last one.
+        wait_copies();
         retire_group(a.mask.queue);
     }
 }
