@@ -267,7 +267,43 @@ def main():
         extra.update({"linear_branch_ms": round(lin_ms, 4),
                       "linear_branch_gbs": round(lbytes / (lin_ms * 1e-3) / 1e9, 1),
                       "linear_branch_pct_hbm": round(100 * lbytes / (lin_ms * 1e-3) / 8e12, 2)})
-        del lout, lws
+
+        # SALAD gate (HBM-bound GEMV over the block input) and output (the
+        # linear branch projected by a C x C weight, gated, added to the
+        # sparse branch: an MFMA GEMM) with synthetic weights; the branch
+        # outputs are this run's sparse and linear outputs
+        B_, H_, N_, D_ = q.shape
+        C_ = H_ * D_
+        sd = workloads.make_salad_inputs(B_, H_, N_, D_, seed=w.seed + 11, device=dev)
+        del sd["o_s"], sd["o_l"]
+        gate = torch.empty(B_, dtype=torch.float32, device=dev)
+        gws = torch.empty(max(256, tra.salad_gate_workspace_bytes(B_, N_)), dtype=torch.uint8, device=dev)
+        sout = torch.empty_like(q)
+
+        def _timed(fn, reps=10):
+            fn()
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            for _ in range(reps):
+                fn()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1) / reps
+
+        gate_ms = _timed(lambda: tra.salad_gate(sd["x"], sd["w_gate"], 0.0, gate=gate, workspace=gws,
+                                                stream=stream))
+        comb_ms = _timed(lambda: tra.salad_combine(out, lout, sd["W"], gate, bias=sd["bias"], out=sout,
+                                                   stream=stream))
+        gbytes = sd["x"].numel() * 2
+        cflops = 2.0 * B_ * N_ * C_ * C_
+        extra.update({"salad_gate_ms": round(gate_ms, 4),
+                      "salad_gate_gbs": round(gbytes / (gate_ms * 1e-3) / 1e9, 1),
+                      "salad_combine_ms": round(comb_ms, 4),
+                      "salad_combine_tflops": round(cflops / (comb_ms * 1e-3) / 1e12, 1),
+                      "salad_combine_pct_bf16_peak": round(100 * cflops / (comb_ms * 1e-3) / 1e12
+                                                           / BF16_PEAK_TFLOPS, 2)})
+        del lout, lws, sd, gate, gws, sout
 
     if w.kind == "swa" and w.dtype == "bf16" and w.s % 128 == 0:
         # frame streaming through the K/V ring: steady state (ring full), one

@@ -268,6 +268,52 @@ size_t tra_linear_attn_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t 
 tra_status tra_linear_attn_fwd(const tra_tensor *Q, const tra_tensor *K, const tra_tensor *V, tra_tensor *O,
                                float eps, void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/*
+ * SALAD gate and output (page "SALAD", section 2.2 for the gate; section 2.1
+ * for the one projection layer the linear branch adds).  The gate scales the
+ * linear branch by one scalar per sample:
+ *     g[b] = (1 / N) sum_n sigmoid(X[b, n, :] . w + bias),
+ * the mean over the tokens of a sigmoid of a learned linear map of the
+ * block input X.  The branch output is then projected and added to the
+ * sparse branch in the merged-head channel space c = h * D + e (C = H * D
+ * channels; channel c of token n is element [b, c / D, n, c % D] of a
+ * [B, H, N, D] tensor):
+ *     out[b, n, c'] = O_sparse[b, n, c'] + g[b] * (sum_c O_lin[b, n, c] W[c', c] + bias[c']).
+ * The weights are the model's (trained) parameters; the library only
+ * applies them.  A caller that drops the linear branch when g is small
+ * reads g back before deciding to call tra_salad_combine.
+ *
+ * tra_salad_gate_workspace_bytes -- device workspace bytes tra_salad_gate
+ *   needs for B samples of N tokens (256-byte multiple).
+ * tra_salad_gate -- X: the block input as a [B, 1, N, C] bf16 view (H = 1,
+ *   D = C channels, C a multiple of 8 and at most 8192; unit channel
+ *   stride; B and N strides multiples of 8 elements; 16-byte aligned);
+ *   w: device bf16 [C], 16-byte aligned; bias: the map's scalar bias;
+ *   gate: device fp32 [B], written; workspace: device memory of at least
+ *   that many bytes, 256-byte aligned, owned by the caller and overwritten.
+ *   fp32 sums in a fixed order (bitwise reproducible).  Asynchronous;
+ *   allocates nothing.  Errors: TRA_ERR_INVALID (null pointer, workspace too
+ *   small or misaligned, N = 0 with B > 0), TRA_ERR_SHAPE (negative sizes,
+ *   H != 1), TRA_ERR_UNSUPPORTED (dtype, C, strides, alignment),
+ *   TRA_ERR_HIP.
+ * tra_salad_combine -- O_sparse, O_lin, out: [B, H, N, D] bf16 views of one
+ *   shape (forward's stride rules, D = 64 or 128, C = H * D a multiple of
+ *   64); W: device bf16 [C][C] row-major (row c' holds the weights of output
+ *   channel c', as a PyTorch Linear weight), 16-byte aligned; bias: device
+ *   fp32 [C], 16-byte aligned, or NULL for none; gate: device fp32 [B] (for
+ *   example from tra_salad_gate).  out may be O_sparse itself (same data
+ *   and strides: every element is read before the same thread writes it),
+ *   never O_lin.  fp32 accumulation; out rounded to bf16.  Asynchronous;
+ *   allocates nothing.  Errors: TRA_ERR_INVALID (null pointer, out sharing
+ *   O_lin's data), TRA_ERR_SHAPE, TRA_ERR_UNSUPPORTED (dtype, D, C, strides,
+ *   alignment, sizes past 2^31 tokens), TRA_ERR_HIP.
+ */
+size_t tra_salad_gate_workspace_bytes(int64_t B, int64_t N);
+tra_status tra_salad_gate(const tra_tensor *X, const void *w, float bias, float *gate, void *workspace,
+                          size_t workspace_bytes, void *hip_stream);
+tra_status tra_salad_combine(const tra_tensor *O_sparse, const tra_tensor *O_lin, const void *W, const float *bias,
+                             const float *gate, tra_tensor *out, void *hip_stream);
+
 /* Copy the host-side summary filled at build time.  No device work. */
 tra_status tra_mask_get_info(const tra_mask *mask, tra_mask_info *out);
 

@@ -21,7 +21,8 @@ import os
 import numpy as np
 import torch
 
-__all__ = ["build_mask", "sparse_attn_fwd", "sparse_attn_bwd", "linear_attn_fwd", "KVCache", "Mask", "TraError", "library_path", "load_library",
+__all__ = ["build_mask", "sparse_attn_fwd", "sparse_attn_bwd", "linear_attn_fwd", "salad_gate", "salad_combine",
+           "KVCache", "Mask", "TraError", "library_path", "load_library",
            "KINDS", "GRANULARITIES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -100,6 +101,12 @@ def load_library():
     lib.tra_linear_attn_fwd.argtypes = [P(TensorDesc), P(TensorDesc), P(TensorDesc), P(TensorDesc),
                                         ctypes.c_float, vp, ctypes.c_size_t, vp]
     lib.tra_linear_attn_fwd.restype = ctypes.c_int
+    lib.tra_salad_gate_workspace_bytes.argtypes = [i64, i64]
+    lib.tra_salad_gate_workspace_bytes.restype = ctypes.c_size_t
+    lib.tra_salad_gate.argtypes = [P(TensorDesc), vp, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+    lib.tra_salad_gate.restype = ctypes.c_int
+    lib.tra_salad_combine.argtypes = [P(TensorDesc), P(TensorDesc), vp, vp, vp, P(TensorDesc), vp]
+    lib.tra_salad_combine.restype = ctypes.c_int
     lib.tra_kvcache_create.argtypes = [i64, i64, i64, i64, ctypes.c_int32, ctypes.c_int32, P(vp)]
     lib.tra_kvcache_create.restype = ctypes.c_int
     lib.tra_kvcache_append.argtypes = [vp, P(TensorDesc), P(TensorDesc), vp]
@@ -353,3 +360,52 @@ def linear_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
 
 def linear_attn_workspace_bytes(B: int, H: int, n: int, D: int) -> int:
     return int(load_library().tra_linear_attn_workspace_bytes(B, H, n, D))
+
+
+def salad_gate(x: torch.Tensor, w: torch.Tensor, bias: float = 0.0, gate: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """SALAD gate on the GPU (see tra_salad_gate): gate[b] = mean over tokens
+    of sigmoid(x[b, n] . w + bias).
+
+    x: [B, N, C] bf16 cuda tensor (the block input); w: [C] bf16.  Returns
+    `gate` ([B] float32, a new tensor by default).
+    """
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("expected x as [B, N, C]")
+    B, N, C = x.shape
+    need = int(lib.tra_salad_gate_workspace_bytes(B, N))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    if gate is None:
+        gate = torch.empty(B, dtype=torch.float32, device=x.device)
+    xd = _desc(x.unsqueeze(1))
+    _check(lib.tra_salad_gate(ctypes.byref(xd), ctypes.c_void_p(w.data_ptr()), float(bias),
+                              ctypes.c_void_p(gate.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
+                              workspace.numel(), _stream_handle(stream)), "tra_salad_gate")
+    return gate
+
+
+def salad_gate_workspace_bytes(B: int, N: int) -> int:
+    return int(load_library().tra_salad_gate_workspace_bytes(B, N))
+
+
+def salad_combine(o_sparse: torch.Tensor, o_lin: torch.Tensor, weight: torch.Tensor, gate: torch.Tensor,
+                  bias: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """SALAD output on the GPU (see tra_salad_combine): out = O_sparse +
+    gate[b] * (O_lin W^T + bias) over the merged-head channels h * D + e.
+
+    o_sparse, o_lin: [B, H, N, D] bf16 cuda tensors; weight: [H*D, H*D] bf16
+    (row = output channel); gate: [B] float32; bias: [H*D] float32 or None.
+    `out` defaults to a new tensor; it may be o_sparse itself.
+    """
+    lib = load_library()
+    if out is None:
+        out = torch.empty(o_sparse.shape, dtype=o_sparse.dtype, device=o_sparse.device)
+    descs = [_desc(t) for t in (o_sparse, o_lin, out)]
+    _check(lib.tra_salad_combine(ctypes.byref(descs[0]), ctypes.byref(descs[1]),
+                                 ctypes.c_void_p(weight.data_ptr()),
+                                 ctypes.c_void_p(None if bias is None else bias.data_ptr()),
+                                 ctypes.c_void_p(gate.data_ptr()), ctypes.byref(descs[2]),
+                                 _stream_handle(stream)), "tra_salad_combine")
+    return out

@@ -7,6 +7,7 @@
 #include <numeric>
 #include <vector>
 
+#include "salad.h"
 #include "tra_internal.h"
 
 namespace {
@@ -854,6 +855,100 @@ tra_status tra_linear_attn_fwd(const tra_tensor *Q, const tra_tensor *K, const t
     return hip_status(tra::launch_linear_attn_bf16(Q->data, Q->stride, K->data, K->stride, V->data, V->stride,
                                                    O->data, O->stride, Q->B, Q->H, Q->N, Q->D, eps, workspace,
                                                    (hipStream_t)hip_stream));
+}
+
+size_t tra_salad_gate_workspace_bytes(int64_t B, int64_t N)
+{
+    if (B < 0 || N < 0)
+        return 0;
+    return tra::salad_gate_workspace_bytes(B, N);
+}
+
+tra_status tra_salad_gate(const tra_tensor *X, const void *w, float bias, float *gate, void *workspace,
+                          size_t workspace_bytes, void *hip_stream)
+{
+    if (X == nullptr)
+        return TRA_ERR_INVALID;
+    if (X->B < 0 || X->N < 0 || X->D < 0 || X->H != 1)
+        return TRA_ERR_SHAPE;
+    if (X->dtype != TRA_BF16)
+        return TRA_ERR_UNSUPPORTED;
+    const int64_t C = X->D;
+    if (C == 0 || C % 8 != 0 || C > 8192)
+        return TRA_ERR_UNSUPPORTED;
+    if (X->stride[3] != 1 || X->stride[0] < 0 || X->stride[0] % 8 != 0 || X->stride[2] < 0 ||
+        X->stride[2] % 8 != 0)
+        return TRA_ERR_UNSUPPORTED;
+    if (X->B == 0)
+        return TRA_OK;
+    if (X->N == 0)
+        return TRA_ERR_INVALID;  // the mean over no tokens is undefined
+    if (X->data == nullptr || w == nullptr || gate == nullptr)
+        return TRA_ERR_INVALID;
+    if (((uintptr_t)X->data) % 16 != 0 || ((uintptr_t)w) % 16 != 0)
+        return TRA_ERR_UNSUPPORTED;
+    if (X->B >= 65536 || X->N >= ((int64_t)1 << 40))
+        return TRA_ERR_UNSUPPORTED;
+    if (workspace == nullptr || workspace_bytes < tra::salad_gate_workspace_bytes(X->B, X->N) ||
+        ((uintptr_t)workspace) % 256 != 0)
+        return TRA_ERR_INVALID;
+    const int64_t sx[2] = {X->stride[0], X->stride[2]};
+    return hip_status(tra::launch_salad_gate(X->data, sx, w, bias, X->B, X->N, C, gate, workspace,
+                                             (hipStream_t)hip_stream));
+}
+
+tra_status tra_salad_combine(const tra_tensor *O_sparse, const tra_tensor *O_lin, const void *W, const float *bias,
+                             const float *gate, tra_tensor *out, void *hip_stream)
+{
+    const tra_tensor *ts[3] = {O_sparse, O_lin, out};
+    for (const tra_tensor *t : ts)
+        if (t == nullptr)
+            return TRA_ERR_INVALID;
+    for (const tra_tensor *t : ts) {
+        if (t->B != O_sparse->B || t->H != O_sparse->H || t->N != O_sparse->N || t->D != O_sparse->D)
+            return TRA_ERR_SHAPE;
+        if (t->B < 0 || t->H < 0 || t->N < 0 || t->D < 0)
+            return TRA_ERR_SHAPE;
+    }
+    for (const tra_tensor *t : ts)
+        if (t->dtype != TRA_BF16)
+            return TRA_ERR_UNSUPPORTED;
+    const int64_t B = O_sparse->B, H = O_sparse->H, N = O_sparse->N, D = O_sparse->D;
+    if (D != 64 && D != 128)
+        return TRA_ERR_UNSUPPORTED;
+    for (const tra_tensor *t : ts) {
+        if (t->stride[3] != 1)
+            return TRA_ERR_UNSUPPORTED;
+        for (int j = 0; j < 3; ++j)
+            if (t->stride[j] < 0 || t->stride[j] % 8 != 0)
+                return TRA_ERR_UNSUPPORTED;
+    }
+    const int64_t C = H * D;
+    if (B == 0 || H == 0 || N == 0)
+        return TRA_OK;
+    if (C % 64 != 0 || C > 65536)
+        return TRA_ERR_UNSUPPORTED;
+    for (const tra_tensor *t : ts)
+        if (t->data == nullptr)
+            return TRA_ERR_INVALID;
+    if (W == nullptr || gate == nullptr)
+        return TRA_ERR_INVALID;
+    if (out->data == O_lin->data)
+        return TRA_ERR_INVALID;
+    if (out->data == O_sparse->data)
+        for (int j = 0; j < 3; ++j)
+            if (out->stride[j] != O_sparse->stride[j])
+                return TRA_ERR_INVALID;
+    for (const tra_tensor *t : ts)
+        if (((uintptr_t)t->data) % 16 != 0)
+            return TRA_ERR_UNSUPPORTED;
+    if (((uintptr_t)W) % 16 != 0 || (bias != nullptr && ((uintptr_t)bias) % 16 != 0))
+        return TRA_ERR_UNSUPPORTED;
+    if (B * N >= ((int64_t)1 << 31))
+        return TRA_ERR_UNSUPPORTED;
+    return hip_status(tra::launch_salad_combine(O_sparse->data, O_sparse->stride, O_lin->data, O_lin->stride,
+                                                out->data, out->stride, W, bias, gate, B, H, N, D,
+                                                (hipStream_t)hip_stream));
 }
 
 }  // extern "C"

@@ -161,3 +161,39 @@ def test_linear_rejects_on_host(lib):
     assert lib.tra_linear_attn_fwd(r(t), r(odd), r(t), r(t), 1e-6, None, 0, None) == -3   # shapes differ
     empty = _tdesc(N=0, data=0)
     assert lib.tra_linear_attn_fwd(r(empty), r(empty), r(empty), r(empty), 1e-6, None, 0, None) == 0
+
+
+def test_salad_rejects_on_host(lib):
+    r = ctypes.byref
+    assert lib.tra_salad_gate_workspace_bytes(-1, 10) == 0
+    assert lib.tra_salad_gate_workspace_bytes(2, 300) % 256 == 0 and lib.tra_salad_gate_workspace_bytes(2, 300) > 0
+    x = _tdesc(B=2, H=1, N=300, D=256)
+    w = ctypes.c_void_p(0x20000)
+    g = ctypes.c_void_p(0x30000)
+    assert lib.tra_salad_gate(None, w, 0.0, g, None, 0, None) == -1
+    assert lib.tra_salad_gate(r(_tdesc(B=2, H=2, N=300, D=256)), w, 0.0, g, None, 0, None) == -3   # H != 1
+    assert lib.tra_salad_gate(r(_tdesc(B=2, H=1, N=300, D=256, dtype=0)), w, 0.0, g, None, 0, None) == -2
+    assert lib.tra_salad_gate(r(_tdesc(B=2, H=1, N=300, D=12)), w, 0.0, g, None, 0, None) == -2    # C % 8
+    assert lib.tra_salad_gate(r(_tdesc(B=2, H=1, N=0, D=256)), w, 0.0, g, None, 0, None) == -1     # mean of none
+    assert lib.tra_salad_gate(r(_tdesc(B=0, H=1, N=5, D=256)), w, 0.0, g, None, 0, None) == 0      # nothing to do
+    assert lib.tra_salad_gate(r(x), None, 0.0, g, None, 0, None) == -1
+    assert lib.tra_salad_gate(r(x), w, 0.0, None, None, 0, None) == -1
+    assert lib.tra_salad_gate(r(_tdesc(B=2, H=1, N=300, D=256, data=0x10002)), w, 0.0, g, None, 0, None) == -2
+    assert lib.tra_salad_gate(r(x), w, 0.0, g, None, 0, None) == -1                                  # no workspace
+
+    t = _tdesc(B=1, H=2, N=300, D=64)
+    other = _tdesc(B=1, H=2, N=300, D=64, data=0x40000)
+    out = _tdesc(B=1, H=2, N=300, D=64, data=0x50000)
+    W = ctypes.c_void_p(0x60000)
+    assert lib.tra_salad_combine(None, r(other), W, None, g, r(out), None) == -1
+    assert lib.tra_salad_combine(r(_tdesc(B=1, H=2, N=300, D=64, dtype=0)), r(other), W, None, g, r(out), None) == -2
+    assert lib.tra_salad_combine(r(t), r(_tdesc(B=1, H=2, N=301, D=64, data=0x40000)), W, None, g, r(out), None) == -3
+    assert lib.tra_salad_combine(r(_tdesc(B=1, H=2, N=300, D=96)), r(_tdesc(B=1, H=2, N=300, D=96, data=0x40000)),
+                                 W, None, g, r(_tdesc(B=1, H=2, N=300, D=96, data=0x50000)), None) == -2  # D
+    assert lib.tra_salad_combine(r(t), r(other), None, None, g, r(out), None) == -1                # no W
+    assert lib.tra_salad_combine(r(t), r(other), W, None, None, r(out), None) == -1                # no gate
+    assert lib.tra_salad_combine(r(t), r(other), W, None, g, r(_tdesc(B=1, H=2, N=300, D=64, data=0x40000)),
+                                 None) == -1                                                        # out is O_lin
+    assert lib.tra_salad_combine(r(t), r(other), W, ctypes.c_void_p(0x70004), g, r(out), None) == -2  # bias align
+    empty = [_tdesc(B=1, H=2, N=0, D=64, data=0) for _ in range(3)]
+    assert lib.tra_salad_combine(r(empty[0]), r(empty[1]), None, None, None, r(empty[2]), None) == 0

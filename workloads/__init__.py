@@ -15,6 +15,8 @@ from __future__ import annotations
 
 from dataclasses import dataclass, field
 
+import math
+
 import torch
 
 
@@ -99,6 +101,34 @@ def make_qkv(w: Workload, device="cpu", seed: int | None = None, heads: int | No
             x = x.to(torch.bfloat16)
         out.append(x)
     return tuple(out)
+
+
+def make_salad_inputs(B: int, H: int, N: int, D: int, seed: int, device="cpu"):
+    """Seeded synthetic inputs of the SALAD gate and output, as a dict.
+
+    One generator on `device`, drawn in this order, all fp32 N(0, 1) before
+    scaling and rounding to bf16 (nearest-even) unless noted:
+      x      [B, N, C]  the block input (C = H * D);
+      w_gate [C]        times 1 / sqrt(C);
+      W      [C, C]     times 1 / sqrt(C) (row = output channel);
+      bias   [C]        times 0.1, kept fp32;
+      o_s    [B, H, N, D] and o_l [B, H, N, D]: stand-ins for the sparse and
+                        linear branch outputs;
+      gate   [B]        uniform in (0, 1), fp32.
+    """
+    C = H * D
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    f32 = dict(generator=g, device=device, dtype=torch.float32)
+    inv = torch.tensor(1.0 / math.sqrt(C), dtype=torch.float32, device=device)
+    x = torch.randn((B, N, C), **f32).to(torch.bfloat16)
+    w_gate = (torch.randn((C,), **f32) * inv).to(torch.bfloat16)
+    W = (torch.randn((C, C), **f32) * inv).to(torch.bfloat16)
+    bias = torch.randn((C,), **f32) * torch.tensor(0.1, dtype=torch.float32, device=device)
+    o_s = torch.randn((B, H, N, D), **f32).to(torch.bfloat16)
+    o_l = torch.randn((B, H, N, D), **f32).to(torch.bfloat16)
+    gate = torch.rand((B,), **f32)
+    return dict(x=x, w_gate=w_gate, W=W, bias=bias, o_s=o_s, o_l=o_l, gate=gate)
 
 
 def to_oracle_array(x: torch.Tensor):
