@@ -87,9 +87,9 @@ __device__ inline void copy_row_vec(const float *x, int row0, int N, float LDS_A
 }
 
 // Byte offsets of a lane's fragments in a swizzled tile.
-//   row_off:  A operand of 32 rows x 16 columns (rows r0 + lane % 32, columns
+//   row:      A operand of 32 rows x 16 columns (rows r0 + lane % 32, columns
 //             16 ks + 8 (lane / 32) ..), one ds_read_b128 per fragment;
-//   tr_off:   A operand of 32 columns x 16 rows read transposed: rows
+//   tr:       A operand of 32 columns x 16 rows read transposed: rows
 //             16 t + 4 (lane / 32) + (lane % 16) / 4 (+ 8 for the second
 //             half), columns 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4).
 template <int D>
@@ -194,15 +194,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void k_bwd_dkdv(BwdArgs a)
 {
     using G = Geo<D>;
-    __shared__ __attribute__((aligned(1024))) char sQ[2 * G::TILE];
-    __shared__ __attribute__((aligned(1024))) char sO[2 * G::TILE];
-    __shared__ __attribute__((aligned(16))) float sL[2][kBlock];
-    __shared__ __attribute__((aligned(16))) float sD[2][kBlock];
+    // double buffers, one LDS array each, named statically in every tile
+    // step: the compiler then tells the copy into one buffer from the reads
+    // of the other and does not wait for the next tile's copy
+    __shared__ __attribute__((aligned(1024))) char sQ0[G::TILE];
+    __shared__ __attribute__((aligned(1024))) char sQ1[G::TILE];
+    __shared__ __attribute__((aligned(1024))) char sO0[G::TILE];
+    __shared__ __attribute__((aligned(1024))) char sO1[G::TILE];
+    __shared__ __attribute__((aligned(16))) float sL0[kBlock];
+    __shared__ __attribute__((aligned(16))) float sL1[kBlock];
+    __shared__ __attribute__((aligned(16))) float sD0[kBlock];
+    __shared__ __attribute__((aligned(16))) float sD1[kBlock];
     __shared__ int sItem;
-    char LDS_AS *lQ = (char LDS_AS *)sQ;
-    char LDS_AS *lO = (char LDS_AS *)sO;
-    float LDS_AS *lL = (float LDS_AS *)&sL[0][0];
-    float LDS_AS *lD = (float LDS_AS *)&sD[0][0];
 
     const AttnArgs &f = a.f;
     const int tid = threadIdx.x;
@@ -214,11 +217,6 @@ void k_bwd_dkdv(BwdArgs a)
     const float c2 = f.scale_log2;
     const float scale = c2 / kLog2e;
 
-    const int crow0 = wave * G::RPI + lane / G::CPR;
-    const int cpc = lane % G::CPR;
-    const int col = (cpc ^ swz<D>(crow0)) * 8;
-    const int64_t offQ = crow0 * f.sq[2] + col;
-    const int64_t offO = crow0 * a.s_do[2] + col;
     typedef const __attribute__((address_space(4))) int32_t cint;
     cint *pair_cols = (cint *)f.mask.t_pair_cols;
     cint *pair_ptr = (cint *)f.mask.t_pair_ptr;
@@ -240,15 +238,21 @@ void k_bwd_dkdv(BwdArgs a)
         const float *Dp = a.delta + (int64_t)bh * N;
         const int key0 = kcol * kBlock + w4 * 32;
 
-        auto copy_all = [&](int u, int buf) {
+        auto copy_all = [&](int u, char LDS_AS *dQ, char LDS_AS *dO, float LDS_AS *dL, float LDS_AS *dD) {
+            // copy geometry recomputed from an opaque lane (a few VALU
+            // operations) rather than held in registers across the loop
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int crow0 = wave * G::RPI + ln / G::CPR;
+            const int col = ((ln % G::CPR) ^ swz<D>(crow0)) * 8;
             const int r0 = u_row[u] * kBlock;
-            copy_tile<D>(Qp, f.sq[2], r0, N, lQ + buf * G::TILE, wave, crow0, col, offQ);
-            copy_tile<D>(Gp, a.s_do[2], r0, N, lO + buf * G::TILE, wave, crow0, col, offO);
-            copy_row_vec(Lp, r0, N, lL + buf * kBlock, wave, 0, lane);
-            copy_row_vec(Dp, r0, N, lD + buf * kBlock, wave, 2, lane);
+            copy_tile<D>(Qp, f.sq[2], r0, N, dQ, wave, crow0, col, crow0 * f.sq[2] + col);
+            copy_tile<D>(Gp, a.s_do[2], r0, N, dO, wave, crow0, col, crow0 * a.s_do[2] + col);
+            copy_row_vec(Lp, r0, N, dL, wave, 0, ln);
+            copy_row_vec(Dp, r0, N, dD, wave, 2, ln);
         };
         if (u0 < u1)
-            copy_all(u0, 0);
+            copy_all(u0, (char LDS_AS *)sQ0, (char LDS_AS *)sO0, (float LDS_AS *)sL0, (float LDS_AS *)sD0);
         // K and V rows of this lane's key as B operands (K^T, V^T fragments)
         bf16x8 kf[G::NKS], vf[G::NKS];
         if (active) {
@@ -266,19 +270,29 @@ void k_bwd_dkdv(BwdArgs a)
             dv[db] = f32x16{};
         }
 
-        for (int u = u0; u < u1; ++u) {
-            const int buf = (u - u0) & 1;
+        // tile u is in buffer (u - u0) & 1; two tiles per trip so that each
+        // step names its buffers statically
+        for (int u2 = u0; u2 < u1; u2 += 2)
+#pragma unroll
+        for (int buf = 0; buf < 2; ++buf) {
+            const int u = u2 + buf;
+            if (u >= u1)
+                break;
             wait_copies();
             __syncthreads();
-            if (u + 1 < u1)
-                copy_all(u + 1, buf ^ 1);
+            // every step issues the same copies (the item's last step
+            // re-copies its tile into the free buffer), so the outstanding
+            // count at each wait is the same on every path
+            copy_all(u + 1 < u1 ? u + 1 : u, (char LDS_AS *)(buf == 0 ? sQ1 : sQ0),
+                     (char LDS_AS *)(buf == 0 ? sO1 : sO0), (float LDS_AS *)(buf == 0 ? sL1 : sL0),
+                     (float LDS_AS *)(buf == 0 ? sD1 : sD0));
             const int em = active ? u_em[2 * u + half] : kAbsent;
             if (em == kAbsent)
                 continue;
-            const char LDS_AS *tQ = lQ + buf * G::TILE;
-            const char LDS_AS *tO = lO + buf * G::TILE;
-            const float LDS_AS *tL = lL + buf * kBlock;
-            const float LDS_AS *tD = lD + buf * kBlock;
+            const char LDS_AS *tQ = (const char LDS_AS *)(buf == 0 ? sQ0 : sQ1);
+            const char LDS_AS *tO = (const char LDS_AS *)(buf == 0 ? sO0 : sO1);
+            const float LDS_AS *tL = (const float LDS_AS *)(buf == 0 ? sL0 : sL1);
+            const float LDS_AS *tD = (const float LDS_AS *)(buf == 0 ? sD0 : sD1);
             // query rows past N (repeated copies of row N - 1) must not count
             const int rows_left = N - u_row[u] * kBlock;
 
@@ -286,7 +300,8 @@ void k_bwd_dkdv(BwdArgs a)
             for (int c = 0; c < 4; ++c) {
                 const int cr = c * 32 * G::ROWB;
                 // fragment offsets are recomputed per chunk (a few VALU
-                // operations) instead of held in 16 registers across the loop
+                // operations) instead of held in 16 registers across the
+                // loop; recomputing them at every use instead costs 25%
                 int ln = lane;
                 asm volatile("" : "+v"(ln));
                 const TileOffsets<D> off(ln);
@@ -301,7 +316,11 @@ void k_bwd_dkdv(BwdArgs a)
                 }
                 // element i of this lane is query 32 c + 8 (i / 4) + 4 hh + i % 4
                 if (em >= 0) {
-                    const uint32_t *mrow = a.f.mask.emask + ((size_t)em * kBlock + c * 32) * 4 + w4;
+                    // base taken opaque in scalar registers here: hoisted, it
+                    // was held in (spilled) vector registers across the loop
+                    const uint32_t *mbase = a.f.mask.emask;
+                    asm volatile("" : "+s"(mbase));
+                    const uint32_t *mrow = mbase + ((size_t)em * kBlock + c * 32) * 4 + w4;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int qi = 8 * (i >> 2) + 4 * hh + (i & 3);
@@ -315,25 +334,28 @@ void k_bwd_dkdv(BwdArgs a)
                         if (c * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) >= rows_left)
                             s[i] = kNegInf;
                 }
+                // four elements (one LSE and one delta vector) at a time
+                bf16x4 pq[4], sq[4];
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const f32x4 lse = *(const f32x4 LDS_AS *)(tL + c * 32 + 8 * r4 + 4 * hh);
+                    const f32x4 dl = *(const f32x4 LDS_AS *)(tD + c * 32 + 8 * r4 + 4 * hh);
+                    f32x4 pv, dsv;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const int i = 4 * r4 + x;
+                        const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse[x] * kLog2e));
+                        pv[x] = p;
+                        dsv[x] = p * (dp[i] - dl[x]);
+                    }
+                    pq[r4] = __builtin_convertvector(pv, bf16x4);
+                    sq[r4] = __builtin_convertvector(dsv, bf16x4);
+                }
                 bf16x8 pb[2], sb[2];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    f32x4 lse[2], dl[2];
-#pragma unroll
-                    for (int r = 0; r < 2; ++r) {
-                        lse[r] = *(const f32x4 LDS_AS *)(tL + c * 32 + 16 * t + 8 * r + 4 * hh);
-                        dl[r] = *(const f32x4 LDS_AS *)(tD + c * 32 + 16 * t + 8 * r + 4 * hh);
-                    }
-                    f32x8 pv, dsv;
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) {
-                        const int i = 8 * t + x;
-                        const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse[x >> 2][x & 3] * kLog2e));
-                        pv[x] = p;
-                        dsv[x] = p * (dp[i] - dl[x >> 2][x & 3]);
-                    }
-                    pb[t] = __builtin_convertvector(pv, bf16x8);
-                    sb[t] = __builtin_convertvector(dsv, bf16x8);
+                    pb[t] = __builtin_shufflevector(pq[2 * t], pq[2 * t + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+                    sb[t] = __builtin_shufflevector(sq[2 * t], sq[2 * t + 1], 0, 1, 2, 3, 4, 5, 6, 7);
                 }
                 // ---- dV^T += dO^T P, dK^T += Q^T dS over the 32 queries ----
 #pragma unroll
@@ -354,6 +376,9 @@ void k_bwd_dkdv(BwdArgs a)
             store_rows_t<D>(dVp, a.s_dv[2], key0 + lq, N, dv, 1.f, hh);
         }
     }
+    // A wave's copies land in issue order, so an item's last (repeated) copy
+    // never overwrites the next item's first; only the workgroup's end waits.
+    wait_copies();
     retire_group(f.mask.queue);
 }
 
@@ -369,11 +394,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void k_bwd_dq(BwdArgs a)
 {
     using G = Geo<D>;
-    __shared__ __attribute__((aligned(1024))) char sK[2 * G::TILE];
-    __shared__ __attribute__((aligned(1024))) char sV[2 * G::TILE];
+    // double buffers, one LDS array each (as in the dK/dV kernel)
+    __shared__ __attribute__((aligned(1024))) char sK0[G::TILE];
+    __shared__ __attribute__((aligned(1024))) char sK1[G::TILE];
+    __shared__ __attribute__((aligned(1024))) char sV0[G::TILE];
+    __shared__ __attribute__((aligned(1024))) char sV1[G::TILE];
     __shared__ int sItem;
-    char LDS_AS *lK = (char LDS_AS *)sK;
-    char LDS_AS *lV = (char LDS_AS *)sV;
 
     const AttnArgs &f = a.f;
     const int tid = threadIdx.x;
@@ -411,8 +437,8 @@ void k_bwd_dq(BwdArgs a)
         const int q0 = row * kBlock + w4 * 32;
 
         if (u0 < u1) {
-            copy_tile<D>(Kp, f.sk[2], u_col[u0] * kBlock, N, lK, wave, crow0, col, offK);
-            copy_tile<D>(Vp, f.sv[2], u_col[u0] * kBlock, N, lV, wave, crow0, col, offV);
+            copy_tile<D>(Kp, f.sk[2], u_col[u0] * kBlock, N, (char LDS_AS *)sK0, wave, crow0, col, offK);
+            copy_tile<D>(Vp, f.sv[2], u_col[u0] * kBlock, N, (char LDS_AS *)sV0, wave, crow0, col, offV);
         }
         bf16x8 qf[G::NKS], gf[G::NKS];
         float lse2 = 0.f, dl = 0.f;
@@ -431,23 +457,36 @@ void k_bwd_dq(BwdArgs a)
         for (int db = 0; db < G::NDB; ++db)
             dq[db] = f32x16{};
 
-        for (int u = u0; u < u1; ++u) {
-            const int buf = (u - u0) & 1;
-            wait_copies();
-            __syncthreads();
-            if (u + 1 < u1) {
-                const int nb = buf ^ 1;
-                copy_tile<D>(Kp, f.sk[2], u_col[u + 1] * kBlock, N, lK + nb * G::TILE, wave, crow0, col, offK);
-                copy_tile<D>(Vp, f.sv[2], u_col[u + 1] * kBlock, N, lV + nb * G::TILE, wave, crow0, col, offV);
-            }
+        // tile u is in buffer (u - u0) & 1; two tiles per trip so that each
+        // step names its buffers statically
+        for (int u2 = u0; u2 < u1; u2 += 2)
+#pragma unroll
+        for (int buf = 0; buf < 2; ++buf) {
+            const int u = u2 + buf;
+            if (u >= u1)
+                break;
+            // the element mask word is loaded under the wait for tile u,
+            // never after the next tile's copies (waiting for it there would
+            // wait for them too)
             const int em = active ? u_em[2 * u + half] : kAbsent;
-            if (em == kAbsent)
-                continue;
-            const char LDS_AS *tK = lK + buf * G::TILE;
-            const char LDS_AS *tV = lV + buf * G::TILE;
             uint4 mw = make_uint4(~0u, ~0u, ~0u, ~0u);
             if (em >= 0)
                 mw = ((const uint4 *)f.mask.emask)[(size_t)em * kBlock + w4 * 32 + lq];
+            wait_copies();
+            __syncthreads();
+            // every step issues the same copies (the item's last step
+            // re-copies its tile into the free buffer)
+            {
+                const int un = u + 1 < u1 ? u + 1 : u;
+                copy_tile<D>(Kp, f.sk[2], u_col[un] * kBlock, N, (char LDS_AS *)(buf == 0 ? sK1 : sK0), wave,
+                             crow0, col, offK);
+                copy_tile<D>(Vp, f.sv[2], u_col[un] * kBlock, N, (char LDS_AS *)(buf == 0 ? sV1 : sV0), wave,
+                             crow0, col, offV);
+            }
+            if (em == kAbsent)
+                continue;
+            const char LDS_AS *tK = (const char LDS_AS *)(buf == 0 ? sK0 : sK1);
+            const char LDS_AS *tV = (const char LDS_AS *)(buf == 0 ? sV0 : sV1);
             const uint32_t words[4] = {mw.x, mw.y, mw.z, mw.w};
 
 #pragma unroll 1
@@ -507,6 +546,7 @@ void k_bwd_dq(BwdArgs a)
             store_rows_t<D>(dQp, a.s_dq[2], q0 + lq, N, dq, scale, hh);
         }
     }
+    wait_copies();  // the last (repeated) copy lands before the workgroup ends
     retire_group(f.mask.queue);
 }
 
