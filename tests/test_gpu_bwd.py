@@ -161,6 +161,26 @@ def test_bwd_deterministic(tra):
         assert torch.equal(a, b)
 
 
+def test_bwd_strided_views(tra):
+    """Q, K, V, O, dO as [B, H, n, D] views of [B, n, H, D] storage and the
+    gradients written into such views give the contiguous run's gradients
+    bit for bit (the kernels take strides, the arithmetic is the same)."""
+    w = workloads.Workload("radial_f6_s256", "radial", "block_any", 6, 256, 2, 3, 128, "bf16", seed=61)
+    mask = tra.build_mask(w.f, w.s, w.kind, **w.mask_kwargs())
+    (q, k, v, do), (dq, dk, dv) = run_bwd(tra, w, mask)
+    out, lse = tra.sparse_attn_fwd(q, k, v, mask)
+    view = lambda x: x.transpose(1, 2).contiguous().transpose(1, 2)
+    qs, ks, vs, os_, dos = (view(x) for x in (q, k, v, out, do))
+    assert not qs.is_contiguous()
+    grads = tuple(torch.empty(w.B, w.n, w.H, w.D, dtype=q.dtype, device="cuda").transpose(1, 2)
+                  for _ in range(3))
+    tra.sparse_attn_bwd(qs, ks, vs, os_, lse, dos, mask, grads=grads)
+    torch.cuda.synchronize()
+    for a, b in zip(grads, (dq, dk, dv)):
+        assert torch.equal(a, b)
+    mask.free()
+
+
 def test_bwd_errors(tra):
     w = workloads.Workload("radial_f4_s128", "radial", "element", 4, 128, 1, 1, 64, "f32", seed=1)
     q, k, v = workloads.make_qkv(w, device="cuda")

@@ -60,3 +60,18 @@ def test_linear_errors(tra):
         tra.linear_attn_fwd(q.float(), q.float(), q.float())
     assert e.value.status == -2
     assert tra.linear_attn_workspace_bytes(1, 1, 128, 96) == 0
+
+
+def test_linear_strided_views(tra):
+    """[B, H, n, D] views of [B, n, H, D] storage (inputs and output) give the
+    contiguous run's output bit for bit."""
+    w = workloads.Workload("lin", "dense", "element", 1, 3000, 2, 3, 128, "bf16", seed=77)
+    q, k, v = workloads.make_qkv(w, device="cuda")
+    ref = tra.linear_attn_fwd(q, k, v)
+    view = lambda x: x.transpose(1, 2).contiguous().transpose(1, 2)
+    qs, ks, vs = (view(x) for x in (q, k, v))
+    assert not qs.is_contiguous()
+    out = torch.empty(2, 3000, 3, 128, dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    tra.linear_attn_fwd(qs, ks, vs, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
