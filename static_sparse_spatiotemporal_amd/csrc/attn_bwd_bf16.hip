@@ -17,9 +17,10 @@
 // Both main kernels recompute S and dP with v_mfma_f32_32x32x16_bf16 and
 // keep the operand that stays fixed for the workgroup (K and V, or Q and dO)
 // in registers; the streamed tiles are copied HBM -> LDS with
-// global_load_lds_dwordx4 into double buffers, XOR-swizzled so that both the
-// row reads (ds_read_b128) and the transposed reads (ds_read_b64_tr_b16) of
-// one tile stay spread over the banks.
+// global_load_lds_dwordx4 into double buffers (one LDS array each, named
+// statically in every step), XOR-swizzled so that both the row reads
+// (ds_read_b128) and the transposed reads (ds_read_b64_tr_b16) of one tile
+// stay spread over the banks.
 #include "attn_common.h"
 
 namespace tra {

@@ -16,9 +16,11 @@
 //   - K and V tiles (128 x D bf16) are double-buffered in LDS (128 KB at
 //     D = 128) and copied HBM -> LDS by global_load_lds_dwordx4 (no register
 //     staging).  The copy of tile u + 1 is issued right after the single
-//     barrier of tile u, so it has a whole tile of compute to land.  An XOR
-//     swizzle of 16-byte chunks keeps the operand reads free of bank
-//     conflicts;
+//     barrier of tile u, so it has a whole tile of compute to land; each
+//     buffer is its own LDS array, named statically in every step, so the
+//     compiler does not hold the reads of tile u back until that copy has
+//     landed.  An XOR swizzle of 16-byte chunks keeps the operand reads free
+//     of bank conflicts;
 //   - scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: a lane holds one query and 64 of the 128 keys
 //     of the tile, so the row max is lane-local plus one permlane32 swap, and
