@@ -429,19 +429,26 @@ __global__ __launch_bounds__(256) void k_merge_splits(AttnArgs a)
 }
 
 // dst[b, h, row0 + r, :] = src[b, h, r, :]; one 16-byte chunk per thread.
-__global__ __launch_bounds__(256) void k_ring_copy(const __bf16 *src, int64_t s0, int64_t s1, int64_t s2,
-                                                  __bf16 *ring, int64_t H, int64_t rows, int64_t D,
+struct RingCopy {
+    const __bf16 *src;
+    int64_t s[3];  // B, H, row strides of the source view
+    __bf16 *ring;
+};
+
+// blockIdx.y = 0 copies K, 1 copies V (one launch per appended frame).
+__global__ __launch_bounds__(256) void k_ring_copy(RingCopy k, RingCopy v, int64_t H, int64_t rows, int64_t D,
                                                   int64_t ring_rows, int64_t row0, int64_t total)
 {
+    const RingCopy &c = blockIdx.y == 0 ? k : v;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= total)
         return;
     const int64_t cpr = D / 8;
-    const int64_t c = t % cpr, rr = t / cpr;
+    const int64_t ch = t % cpr, rr = t / cpr;
     const int64_t r = rr % rows, bh = rr / rows;
     const int64_t b = bh / H, h = bh - b * H;
-    const bf16x8 v = *(const bf16x8 *)(src + b * s0 + h * s1 + r * s2 + 8 * c);
-    *(bf16x8 *)(ring + (bh * ring_rows + row0 + r) * D + 8 * c) = v;
+    const bf16x8 val = *(const bf16x8 *)(c.src + b * c.s[0] + h * c.s[1] + r * c.s[2] + 8 * ch);
+    *(bf16x8 *)(c.ring + (bh * ring_rows + row0 + r) * D + 8 * ch) = val;
 }
 
 }  // namespace
@@ -472,14 +479,17 @@ hipError_t launch_attn_stream_bf16(const AttnArgs &a, hipStream_t st)
     return hipGetLastError();
 }
 
-hipError_t launch_ring_copy(const void *src, const int64_t *s_src, void *ring, int64_t B, int64_t H, int64_t rows,
-                            int64_t D, int64_t ring_rows, int64_t row0, hipStream_t st)
+hipError_t launch_ring_copy(const void *k_src, const int64_t *s_k, void *ring_k, const void *v_src,
+                            const int64_t *s_v, void *ring_v, int64_t B, int64_t H, int64_t rows, int64_t D,
+                            int64_t ring_rows, int64_t row0, hipStream_t st)
 {
     const int64_t total = B * H * rows * (D / 8);
     if (total == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(k_ring_copy, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, (const __bf16 *)src,
-                       s_src[0], s_src[1], s_src[2], (__bf16 *)ring, H, rows, D, ring_rows, row0, total);
+    RingCopy k{(const __bf16 *)k_src, {s_k[0], s_k[1], s_k[2]}, (__bf16 *)ring_k};
+    RingCopy v{(const __bf16 *)v_src, {s_v[0], s_v[1], s_v[2]}, (__bf16 *)ring_v};
+    hipLaunchKernelGGL(k_ring_copy, dim3((unsigned)((total + 255) / 256), 2), dim3(256), 0, st, k, v, H, rows, D,
+                       ring_rows, row0, total);
     return hipGetLastError();
 }
 

@@ -710,9 +710,8 @@ tra_status tra_kvcache_append(tra_kvcache *c, const tra_tensor *K, const tra_ten
     const int64_t ring_rows = (int64_t)c->window * c->s;
     const int64_t row0 = (c->appended % c->window) * c->s;
     hipStream_t hs = (hipStream_t)hip_stream;
-    hipError_t e = tra::launch_ring_copy(K->data, K->stride, c->ring_k, c->B, c->H, c->s, c->D, ring_rows, row0, hs);
-    if (e == hipSuccess)
-        e = tra::launch_ring_copy(V->data, V->stride, c->ring_v, c->B, c->H, c->s, c->D, ring_rows, row0, hs);
+    const hipError_t e = tra::launch_ring_copy(K->data, K->stride, c->ring_k, V->data, V->stride, c->ring_v, c->B,
+                                               c->H, c->s, c->D, ring_rows, row0, hs);
     if (e != hipSuccess)
         return hip_status(e);
     c->appended++;

@@ -134,10 +134,11 @@ struct AttnArgs {
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t st);
 // Split-key launch (see AttnArgs) followed by the merge into a.o / a.lse.
 hipError_t launch_attn_stream_bf16(const AttnArgs &a, hipStream_t st);
-// Copy a [B, H, rows, D] bf16 view into rows row0 .. of a contiguous
-// [B, H, ring_rows, D] buffer.
-hipError_t launch_ring_copy(const void *src, const int64_t *s_src, void *ring, int64_t B, int64_t H, int64_t rows,
-                            int64_t D, int64_t ring_rows, int64_t row0, hipStream_t st);
+// Copy two [B, H, rows, D] bf16 views (K and V) into rows row0 .. of their
+// contiguous [B, H, ring_rows, D] buffers, in one launch.
+hipError_t launch_ring_copy(const void *k_src, const int64_t *s_k, void *ring_k, const void *v_src,
+                            const int64_t *s_v, void *ring_v, int64_t B, int64_t H, int64_t rows, int64_t D,
+                            int64_t ring_rows, int64_t row0, hipStream_t st);
 hipError_t launch_attn_f32(const AttnArgs &a, hipStream_t st);
 
 // Attention backward (attn_bwd_bf16.hip): gradients of eq. 2 from the saved
