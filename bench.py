@@ -228,14 +228,14 @@ def main():
         dout = torch.randn(q.shape, generator=g, device=dev).to(torch.bfloat16)
         tra.sparse_attn_fwd(q, k, v, bmask, out=out, lse=lse, stream=stream)
         grads = tuple(torch.empty_like(q) for _ in range(3))
-        delta = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-        tra.sparse_attn_bwd(q, k, v, out, lse, dout, bmask, grads=grads, delta=delta, stream=stream)
+        ws = torch.empty(tra.sparse_attn_bwd_workspace_bytes(*q.shape), dtype=torch.uint8, device=dev)
+        tra.sparse_attn_bwd(q, k, v, out, lse, dout, bmask, grads=grads, workspace=ws, stream=stream)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = 5
         e0.record(stream)
         for _ in range(reps):
-            tra.sparse_attn_bwd(q, k, v, out, lse, dout, bmask, grads=grads, delta=delta, stream=stream)
+            tra.sparse_attn_bwd(q, k, v, out, lse, dout, bmask, grads=grads, workspace=ws, stream=stream)
         e1.record(stream)
         torch.cuda.synchronize()
         bwd_ms = e0.elapsed_time(e1) / reps
@@ -246,7 +246,7 @@ def main():
                       "bwd_mfma_tflops_7gemm": round(3.5 * flops_blocks / (bwd_ms * 1e-3) / 1e12, 2),
                       "bwd_pct_bf16_peak_7gemm": round(100 * 3.5 * flops_blocks / (bwd_ms * 1e-3) / 1e12
                                                        / BF16_PEAK_TFLOPS, 2)})
-        del grads, delta, dout
+        del grads, ws, dout
         bmask.free()
 
     if not args.no_bwd and w.dtype == "bf16" and name == workloads.HEADLINE:

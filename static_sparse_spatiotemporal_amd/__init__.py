@@ -21,7 +21,7 @@ import os
 import numpy as np
 import torch
 
-__all__ = ["build_mask", "sparse_attn_fwd", "sparse_attn_bwd", "linear_attn_fwd", "salad_gate", "salad_combine",
+__all__ = ["build_mask", "sparse_attn_fwd", "sparse_attn_bwd", "sparse_attn_bwd_workspace_bytes", "linear_attn_fwd", "salad_gate", "salad_combine",
            "KVCache", "Mask", "TraError", "library_path", "load_library",
            "KINDS", "GRANULARITIES"]
 
@@ -91,11 +91,13 @@ def load_library():
     lib.tra_sparse_attn_fwd.argtypes = [P(TensorDesc), P(TensorDesc), P(TensorDesc), vp, P(TensorDesc),
                                         vp, ctypes.c_float, vp]
     lib.tra_sparse_attn_fwd.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.tra_sparse_attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.tra_sparse_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.tra_sparse_attn_bwd.argtypes = [P(TensorDesc), P(TensorDesc), P(TensorDesc), P(TensorDesc),
                                         P(TensorDesc), vp, vp, P(TensorDesc), P(TensorDesc), P(TensorDesc),
-                                        vp, ctypes.c_float, vp]
+                                        vp, ctypes.c_size_t, ctypes.c_float, vp]
     lib.tra_sparse_attn_bwd.restype = ctypes.c_int
-    i64 = ctypes.c_int64
     lib.tra_linear_attn_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.tra_linear_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.tra_linear_attn_fwd.argtypes = [P(TensorDesc), P(TensorDesc), P(TensorDesc), P(TensorDesc),
@@ -254,27 +256,34 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mas
 
 def sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
                     dout: torch.Tensor, mask: Mask, scale: float | None = None, grads=None,
-                    delta: torch.Tensor | None = None, stream=None):
+                    workspace: torch.Tensor | None = None, stream=None):
     """Gradients (dQ, dK, dV) of sparse_attn_fwd on the GPU (see tra_sparse_attn_bwd).
 
     q, k, v, out, dout: [B, H, n, D] bf16 cuda tensors; lse: the forward's
     [B, H, n] fp32 output.  `grads` = (dq, dk, dv) output tensors (default:
-    new contiguous ones); `delta` a [B, H, n] fp32 workspace (default: new).
+    new contiguous ones); `workspace` a uint8 cuda tensor of at least
+    sparse_attn_bwd_workspace_bytes bytes (default: new).
     """
+    lib = load_library()
+    B, H, n, D = q.shape
     if grads is None:
         grads = tuple(torch.empty(q.shape, dtype=q.dtype, device=q.device) for _ in range(3))
-    if delta is None:
-        delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    for t in (lse, delta):
-        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(q.shape[:3]):
-            raise ValueError("lse and delta must be contiguous float32 [B, H, n] tensors")
+    if workspace is None:
+        workspace = torch.empty(int(lib.tra_sparse_attn_bwd_workspace_bytes(B, H, n, D)), dtype=torch.uint8,
+                                device=q.device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must be a contiguous float32 [B, H, n] tensor")
     descs = [_desc(t) for t in (q, k, v, out, dout)]
     gd = [_desc(t) for t in grads]
-    _check(load_library().tra_sparse_attn_bwd(
+    _check(lib.tra_sparse_attn_bwd(
         *(ctypes.byref(d) for d in descs), ctypes.c_void_p(lse.data_ptr()), mask.handle,
-        *(ctypes.byref(d) for d in gd), ctypes.c_void_p(delta.data_ptr()),
+        *(ctypes.byref(d) for d in gd), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
         float(scale) if scale else 0.0, _stream_handle(stream)), "tra_sparse_attn_bwd")
     return grads
+
+
+def sparse_attn_bwd_workspace_bytes(B: int, H: int, n: int, D: int) -> int:
+    return int(load_library().tra_sparse_attn_bwd_workspace_bytes(B, H, n, D))
 
 
 class KVCache:

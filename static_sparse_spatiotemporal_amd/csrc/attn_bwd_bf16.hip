@@ -5,18 +5,23 @@
 // delta = rowsum(dO o O) = rowsum(P o dP):
 //   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - delta),
 //   dK = scale dS^T Q,   dQ = scale dS K.
+// P is recomputed exactly as the forward computed it: from the queries
+// multiplied by scale * log2(e) and rounded to bf16 (Qs), in units of log2,
+// so that its rows sum to 1 against the forward's LSE.  Then
+// scale Q = ln 2 Qs up to that rounding, and dK = ln 2 dS^T Qs.
 // Three kernels, no atomics (results are deterministic):
-//   k_bwd_delta  delta per row;
+//   k_bwd_prep   per row: delta, -LSE log2(e) and the row of Qs (workspace);
 //   k_bwd_dkdv   one workgroup per pair of key blocks (the mask's schedule
-//                over key blocks), 8 waves x 32 keys; streams the Q and dO
+//                over key blocks), 8 waves x 32 keys; streams the Qs and dO
 //                tiles of every query block that keeps one of its key blocks
 //                and accumulates dK and dV in registers;
 //   k_bwd_dq     one workgroup per pair of query blocks (the forward's
 //                schedule), 8 waves x 32 queries; streams K and V tiles and
 //                accumulates dQ.
-// Both main kernels recompute S and dP with v_mfma_f32_32x32x16_bf16 and
-// keep the operand that stays fixed for the workgroup (K and V, or Q and dO)
-// in registers; the streamed tiles are copied HBM -> LDS with
+// Both main kernels recompute S and dP with v_mfma_f32_32x32x16_bf16, the S
+// products starting from -LSE log2(e) instead of 0 (their output goes
+// straight into v_exp_f32), and keep the operand that stays fixed for the
+// workgroup (K and V, or Qs and dO) in registers; the streamed tiles are copied HBM -> LDS with
 // global_load_lds_dwordx4 into double buffers (one LDS array each, named
 // statically in every step), XOR-swizzled so that both the row reads
 // (ds_read_b128) and the transposed reads (ds_read_b64_tr_b16) of one tile
@@ -150,36 +155,47 @@ __device__ inline void store_rows_t(__bf16 *X, int64_t stride, int row, int N, c
         }
 }
 
-// ---------------------------------------------------------------- delta
+// ---------------------------------------------------------------- prep
 
-// delta[row] = sum_d dO[row, d] O[row, d]; 8 lanes per row.
+// Per row r = (b, h, q), 8 lanes per row: delta[r] = sum_d dO[r, d] O[r, d],
+// nlse2[r] = -LSE[r] log2(e) (-inf for an empty row, whose probabilities
+// are then 0), and qs[r, :] = bf16(Q[r, :] * scale log2(e)) as the forward
+// rounds it, rows of D contiguous elements.
 template <int D>
-__global__ __launch_bounds__(256) void k_bwd_delta(BwdArgs a)
+__global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a)
 {
     constexpr int PER = D / 8;  // elements per lane
     const int64_t rows = (int64_t)a.f.B * a.f.H * a.f.N;
     const int64_t r = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
     const int part = threadIdx.x & 7;
+    const float c2 = a.f.scale_log2;
     float acc = 0.f;
     if (r < rows) {
         const int64_t bh = r / a.f.N, q = r - bh * a.f.N;
         const int64_t b = bh / a.f.H, h = bh - b * a.f.H;
         const __bf16 *o = (const __bf16 *)a.o + b * a.s_o[0] + h * a.s_o[1] + q * a.s_o[2] + part * PER;
         const __bf16 *g = (const __bf16 *)a.dout + b * a.s_do[0] + h * a.s_do[1] + q * a.s_do[2] + part * PER;
+        const __bf16 *x = (const __bf16 *)a.f.q + b * a.f.sq[0] + h * a.f.sq[1] + q * a.f.sq[2] + part * PER;
+        __bf16 *xs = (__bf16 *)a.qs + r * D + part * PER;
 #pragma unroll
         for (int c = 0; c < PER / 8; ++c) {
             const bf16x8 ov = *(const bf16x8 *)(o + 8 * c);
             const bf16x8 gv = *(const bf16x8 *)(g + 8 * c);
 #pragma unroll
-            for (int x = 0; x < 8; ++x)
-                acc = fmaf((float)ov[x], (float)gv[x], acc);
+            for (int e = 0; e < 8; ++e)
+                acc = fmaf((float)ov[e], (float)gv[e], acc);
+            const bf16x8 xv = *(const bf16x8 *)(x + 8 * c);
+            *(bf16x8 *)(xs + 8 * c) = __builtin_convertvector(__builtin_convertvector(xv, f32x8) * c2, bf16x8);
         }
     }
     acc += __shfl_xor(acc, 1);
     acc += __shfl_xor(acc, 2);
     acc += __shfl_xor(acc, 4);
-    if (r < rows && part == 0)
+    if (r < rows && part == 0) {
         a.delta[r] = acc;
+        const float l = a.lse[r];
+        a.nlse2[r] = l == kNegInf ? kNegInf : -l * kLog2e;
+    }
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -187,9 +203,9 @@ __global__ __launch_bounds__(256) void k_bwd_delta(BwdArgs a)
 // Workgroup = pair of key blocks; waves 0-3 own the first, 4-7 the second,
 // 32 keys each.  Per query tile and 32-query chunk c (lane = key, 16 queries
 // 32 c + 8 (i / 4) + 4 (lane / 32) + i % 4 per lane):
-//   S = Q K^T and dP = dO V^T with K, V as register B operands;
-//   P = 2^(S scale log2 e - LSE log2 e), dS = P (dP - delta);
-//   dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read transposed.
+//   S = Qs K^T - LSE log2 e and dP = dO V^T with K, V as register B operands;
+//   P = 2^S, dS = P (dP - delta);
+//   dV^T += dO^T P and dK^T += Qs^T dS with dO^T, Qs^T read transposed.
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_bwd_dkdv(BwdArgs a)
@@ -215,8 +231,6 @@ void k_bwd_dkdv(BwdArgs a)
     const int half = wave >> 2, w4 = wave & 3;
     const int lq = lane & 31, hh = lane >> 5;
     const int N = f.N;
-    const float c2 = f.scale_log2;
-    const float scale = c2 / kLog2e;
 
     typedef const __attribute__((address_space(4))) int32_t cint;
     cint *pair_cols = (cint *)f.mask.t_pair_cols;
@@ -231,11 +245,11 @@ void k_bwd_dkdv(BwdArgs a)
         const bool active = kcol >= 0;
         const int u0 = pair_ptr[pair], u1 = pair_ptr[pair + 1];
         const int b = bh / f.H, h = bh - b * f.H;
-        const __bf16 *Qp = (const __bf16 *)f.q + b * f.sq[0] + h * f.sq[1];
+        const __bf16 *Qp = (const __bf16 *)a.qs + (int64_t)bh * N * D;
         const __bf16 *Kp = (const __bf16 *)f.k + b * f.sk[0] + h * f.sk[1];
         const __bf16 *Vp = (const __bf16 *)f.v + b * f.sv[0] + h * f.sv[1];
         const __bf16 *Gp = (const __bf16 *)a.dout + b * a.s_do[0] + h * a.s_do[1];
-        const float *Lp = a.lse + (int64_t)bh * N;
+        const float *Lp = a.nlse2 + (int64_t)bh * N;
         const float *Dp = a.delta + (int64_t)bh * N;
         const int key0 = kcol * kBlock + w4 * 32;
 
@@ -247,7 +261,7 @@ void k_bwd_dkdv(BwdArgs a)
             const int crow0 = wave * G::RPI + ln / G::CPR;
             const int col = ((ln % G::CPR) ^ swz<D>(crow0)) * 8;
             const int r0 = u_row[u] * kBlock;
-            copy_tile<D>(Qp, f.sq[2], r0, N, dQ, wave, crow0, col, crow0 * f.sq[2] + col);
+            copy_tile<D>(Qp, D, r0, N, dQ, wave, crow0, col, crow0 * D + col);
             copy_tile<D>(Gp, a.s_do[2], r0, N, dO, wave, crow0, col, crow0 * a.s_do[2] + col);
             copy_row_vec(Lp, r0, N, dL, wave, 0, ln);
             copy_row_vec(Dp, r0, N, dD, wave, 2, ln);
@@ -306,16 +320,24 @@ void k_bwd_dkdv(BwdArgs a)
                 int ln = lane;
                 asm volatile("" : "+v"(ln));
                 const TileOffsets<D> off(ln);
-                // ---- S = Q K^T and dP = dO V^T (32 queries x 32 keys) ----
-                f32x16 s = f32x16{}, dp = f32x16{};
+                // ---- S = Qs K^T - LSE log2 e, dP = dO V^T (32 queries x 32 keys) ----
+                // element i of this lane is query 32 c + 8 (i / 4) + 4 hh + i % 4
+                f32x16 s0;
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const f32x4 nl = *(const f32x4 LDS_AS *)(tL + c * 32 + 8 * r4 + 4 * hh);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        s0[4 * r4 + x] = nl[x];
+                }
+                f32x16 s, dp = f32x16{};
 #pragma unroll
                 for (int ks = 0; ks < G::NKS; ++ks) {
                     const bf16x8 qa = *(const bf16x8 LDS_AS *)(tQ + cr + off.row[ks]);
                     const bf16x8 ga = *(const bf16x8 LDS_AS *)(tO + cr + off.row[ks]);
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], ks == 0 ? s0 : s, 0, 0, 0);
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
                 }
-                // element i of this lane is query 32 c + 8 (i / 4) + 4 hh + i % 4
                 if (em >= 0) {
                     // base taken opaque in scalar registers here: hoisted, it
                     // was held in (spilled) vector registers across the loop
@@ -335,17 +357,16 @@ void k_bwd_dkdv(BwdArgs a)
                         if (c * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) >= rows_left)
                             s[i] = kNegInf;
                 }
-                // four elements (one LSE and one delta vector) at a time
+                // four elements (one delta vector) at a time
                 bf16x4 pq[4], sq[4];
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    const f32x4 lse = *(const f32x4 LDS_AS *)(tL + c * 32 + 8 * r4 + 4 * hh);
                     const f32x4 dl = *(const f32x4 LDS_AS *)(tD + c * 32 + 8 * r4 + 4 * hh);
                     f32x4 pv, dsv;
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
                         const int i = 4 * r4 + x;
-                        const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lse[x] * kLog2e));
+                        const float p = __builtin_amdgcn_exp2f(s[i]);
                         pv[x] = p;
                         dsv[x] = p * (dp[i] - dl[x]);
                     }
@@ -358,7 +379,7 @@ void k_bwd_dkdv(BwdArgs a)
                     pb[t] = __builtin_shufflevector(pq[2 * t], pq[2 * t + 1], 0, 1, 2, 3, 4, 5, 6, 7);
                     sb[t] = __builtin_shufflevector(sq[2 * t], sq[2 * t + 1], 0, 1, 2, 3, 4, 5, 6, 7);
                 }
-                // ---- dV^T += dO^T P, dK^T += Q^T dS over the 32 queries ----
+                // ---- dV^T += dO^T P, dK^T += Qs^T dS over the 32 queries ----
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -373,7 +394,7 @@ void k_bwd_dkdv(BwdArgs a)
         if (active) {
             __bf16 *dKp = (__bf16 *)a.dk + b * a.s_dk[0] + h * a.s_dk[1];
             __bf16 *dVp = (__bf16 *)a.dv + b * a.s_dv[0] + h * a.s_dv[1];
-            store_rows_t<D>(dKp, a.s_dk[2], key0 + lq, N, dk, scale, hh);
+            store_rows_t<D>(dKp, a.s_dk[2], key0 + lq, N, dk, kLn2, hh);
             store_rows_t<D>(dVp, a.s_dv[2], key0 + lq, N, dv, 1.f, hh);
         }
     }
@@ -387,8 +408,8 @@ void k_bwd_dkdv(BwdArgs a)
 
 // Workgroup = pair of query blocks (the forward's schedule); 32 queries per
 // wave.  Per key tile and 64-key half (lane = query, 32 keys per lane):
-//   S^T = K Q^T and dP^T = V dO^T with Q, dO as register B operands;
-//   P = 2^(S scale log2 e - LSE log2 e), dS = P (dP - delta);
+//   S^T = K Qs^T - LSE log2 e and dP^T = V dO^T with Qs, dO as register B
+//   operands; P = 2^S, dS = P (dP - delta);
 //   dQ^T += K^T dS^T with K^T read transposed.
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -409,8 +430,7 @@ void k_bwd_dq(BwdArgs a)
     const int half = wave >> 2, w4 = wave & 3;
     const int lq = lane & 31, hh = lane >> 5;
     const int N = f.N;
-    const float c2 = f.scale_log2;
-    const float scale = c2 / kLog2e;
+    const float scale = f.scale_log2 / kLog2e;
     const TileOffsets<D> off(lane);
 
     const int crow0 = wave * G::RPI + lane / G::CPR;
@@ -431,7 +451,7 @@ void k_bwd_dq(BwdArgs a)
         const bool active = row >= 0;
         const int u0 = pair_ptr[pair], u1 = pair_ptr[pair + 1];
         const int b = bh / f.H, h = bh - b * f.H;
-        const __bf16 *Qp = (const __bf16 *)f.q + b * f.sq[0] + h * f.sq[1];
+        const __bf16 *Qp = (const __bf16 *)a.qs + (int64_t)bh * N * D;
         const __bf16 *Kp = (const __bf16 *)f.k + b * f.sk[0] + h * f.sk[1];
         const __bf16 *Vp = (const __bf16 *)f.v + b * f.sv[0] + h * f.sv[1];
         const __bf16 *Gp = (const __bf16 *)a.dout + b * a.s_do[0] + h * a.s_do[1];
@@ -442,15 +462,15 @@ void k_bwd_dq(BwdArgs a)
             copy_tile<D>(Vp, f.sv[2], u_col[u0] * kBlock, N, (char LDS_AS *)sV0, wave, crow0, col, offV);
         }
         bf16x8 qf[G::NKS], gf[G::NKS];
-        float lse2 = 0.f, dl = 0.f;
+        float nl = 0.f, dl = 0.f;
         if (active) {
             const int qr = q0 + lq < N ? q0 + lq : N - 1;
 #pragma unroll
             for (int ks = 0; ks < G::NKS; ++ks) {
-                qf[ks] = *(const bf16x8 *)(Qp + (int64_t)qr * f.sq[2] + ks * 16 + hh * 8);
+                qf[ks] = *(const bf16x8 *)(Qp + (int64_t)qr * D + ks * 16 + hh * 8);
                 gf[ks] = *(const bf16x8 *)(Gp + (int64_t)qr * a.s_do[2] + ks * 16 + hh * 8);
             }
-            lse2 = a.lse[(int64_t)bh * N + qr] * kLog2e;
+            nl = a.nlse2[(int64_t)bh * N + qr];
             dl = a.delta[(int64_t)bh * N + qr];
         }
         f32x16 dq[G::NDB];
@@ -492,13 +512,15 @@ void k_bwd_dq(BwdArgs a)
 
 #pragma unroll 1
             for (int hf = 0; hf < 2; ++hf) {
-                // ---- S^T = K Q^T, dP^T = V dO^T: 64 keys x 32 queries ----
+                // ---- S^T = K Qs^T - LSE log2 e, dP^T = V dO^T: 64 keys x 32 queries ----
+                // rebuilt here (held across the loop it costs 16 registers)
+                float nlr = nl;
+                asm volatile("" : "+v"(nlr));
+                const f32x16 s0 = f32x16{} + nlr;
                 f32x16 s[2], dp[2];
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    s[kb] = f32x16{};
+                for (int kb = 0; kb < 2; ++kb)
                     dp[kb] = f32x16{};
-                }
 #pragma unroll
                 for (int ks = 0; ks < G::NKS; ++ks)
 #pragma unroll
@@ -506,7 +528,7 @@ void k_bwd_dq(BwdArgs a)
                         const int ro = (2 * hf + kb) * 32 * G::ROWB + off.row[ks];
                         const bf16x8 ka = *(const bf16x8 LDS_AS *)(tK + ro);
                         const bf16x8 va = *(const bf16x8 LDS_AS *)(tV + ro);
-                        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[kb], 0, 0, 0);
+                        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? s0 : s[kb], 0, 0, 0);
                         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], dp[kb], 0, 0, 0);
                     }
                 // element i of s[kb] is key 32 (2 hf + kb) + 8 (i / 4) + 4 hh + i % 4
@@ -527,7 +549,7 @@ void k_bwd_dq(BwdArgs a)
 #pragma unroll
                     for (int x = 0; x < 8; ++x) {
                         const int i = 8 * (t & 1) + x;
-                        const float p = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][i], c2, -lse2));
+                        const float p = __builtin_amdgcn_exp2f(s[t >> 1][i]);
                         dsv[x] = p * (dp[t >> 1][i] - dl);
                     }
                     sb[t] = __builtin_convertvector(dsv, bf16x8);
@@ -576,14 +598,26 @@ hipError_t launch_persistent_bwd(Kern kern, long long items, const BwdArgs &a, h
 
 }  // namespace
 
+BwdWorkspace bwd_workspace(int64_t B, int64_t H, int64_t N, int64_t D)
+{
+    const auto round = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t rows = (size_t)(B * H * N);
+    BwdWorkspace w;
+    w.delta = 0;
+    w.nlse2 = round(rows * sizeof(float));
+    w.qs = w.nlse2 + round(rows * sizeof(float));
+    w.bytes = w.qs + round(rows * (size_t)D * 2);
+    return w;
+}
+
 hipError_t launch_attn_bwd_bf16(const BwdArgs &a, hipStream_t st)
 {
     const long long rows = (long long)a.f.B * a.f.H * a.f.N;
     const unsigned grid = (unsigned)((rows + 31) / 32);
     if (a.f.D == 128)
-        hipLaunchKernelGGL(k_bwd_delta<128>, dim3(grid), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_bwd_prep<128>, dim3(grid), dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL(k_bwd_delta<64>, dim3(grid), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_bwd_prep<64>, dim3(grid), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

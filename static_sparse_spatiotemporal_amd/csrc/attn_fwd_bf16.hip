@@ -5,7 +5,13 @@
 // eq. 2) over the kept 128 x 128 blocks of the static mask, with the
 // streaming softmax: running row maximum m and denominator l, the
 // accumulator rescaled by 2^(m_old - m_new) when the maximum grows.  Scores
-// are multiplied by scale * log2(e) so that exp is v_exp_f32 (base 2).
+// are taken in units of log2 so that exp is v_exp_f32 (base 2): each query
+// is multiplied by scale * log2(e) once, when its fragments are loaded, and
+// rounded back to bf16 (relative error <= 2^-8 per element, so a score
+// q.k * scale moves by at most 2^-8 * scale * sum_i |q_i k_i|, and the LSE
+// by at most the largest such move over the row).  The score MFMAs start
+// from -m, the row maximum in use, instead of from 0, so that their output
+// goes straight into v_exp_f32 with no per-score VALU work before it.
 //
 // Mapping.  One workgroup = 8 wave64s (two per SIMD) = one work item of the
 // mask's pair schedule: two 128-query blocks whose kept key blocks largely
@@ -176,14 +182,18 @@ void attn_fwd_bf16(AttnArgs a)
         if (active) {
             const int qr = q0 + lq < N ? q0 + lq : N - 1;
 #pragma unroll
-            for (int ks = 0; ks < G::NKS; ++ks)
-                qf[ks] = *(const bf16x8 *)(Qp + (int64_t)qr * a.sq[2] + ks * 16 + hh * 8);
+            for (int ks = 0; ks < G::NKS; ++ks) {
+                const bf16x8 raw = *(const bf16x8 *)(Qp + (int64_t)qr * a.sq[2] + ks * 16 + hh * 8);
+                qf[ks] = __builtin_convertvector(__builtin_convertvector(raw, f32x8) * c2, bf16x8);
+            }
         }
         f32x16 o[G::NDB];
 #pragma unroll
         for (int db = 0; db < G::NDB; ++db)
             o[db] = f32x16{};
-        float m = kNegInf, l = 0.f;
+        // m: row maximum (log2 units), l: row sum; muse: the maximum the
+        // scores are taken relative to (0 while m is -inf).
+        float m = kNegInf, l = 0.f, muse = 0.f;
 
         // Tile u is in buffer (u - u0) & 1; the loop takes two tiles per
         // trip so that the buffer of each step is a constant.
@@ -219,11 +229,9 @@ void attn_fwd_bf16(AttnArgs a)
             const char LDS_AS *tK = (const char LDS_AS *)(buf == 0 ? sK0 : sK1);
             const char LDS_AS *tV = (const char LDS_AS *)(buf == 0 ? sV0 : sV1);
 
-            // ---- S^T = K Q^T: 128 keys x 32 queries ----
+            // ---- S^T = K Q^T - muse: 128 keys x 32 queries ----
             f32x16 s[4];
-#pragma unroll
-            for (int kb4 = 0; kb4 < 4; ++kb4)
-                s[kb4] = f32x16{};
+            const f32x16 s0 = f32x16{} - muse;
             bf16x8 kf[2][4];
 #pragma unroll
             for (int kb4 = 0; kb4 < 4; ++kb4)
@@ -238,7 +246,8 @@ void attn_fwd_bf16(AttnArgs a)
                 }
 #pragma unroll
                 for (int kb4 = 0; kb4 < 4; ++kb4)
-                    s[kb4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks & 1][kb4], qf[ks], s[kb4], 0, 0, 0);
+                    s[kb4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks & 1][kb4], qf[ks], ks == 0 ? s0 : s[kb4],
+                                                                     0, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
 
@@ -261,7 +270,7 @@ void attn_fwd_bf16(AttnArgs a)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     mx = fmaxf(mx, s[kb4][i]);
-            const float mt = lane_pair_max(mx) * c2;
+            const float mt = lane_pair_max(mx) + muse;
             if (__builtin_amdgcn_ballot_w64(mt > m + kTau)) {
                 const float mn = fmaxf(m, mt);
                 const float alpha = __builtin_amdgcn_exp2f(m - (mn == kNegInf ? 0.f : mn));
@@ -270,8 +279,14 @@ void attn_fwd_bf16(AttnArgs a)
                     o[db] *= alpha;
                 l *= alpha;
                 m = mn;
+                // re-base this tile's scores on the new maximum
+                const float mu = m == kNegInf ? 0.f : m;
+                const float dm = mu - muse;
+                muse = mu;
+#pragma unroll
+                for (int kb4 = 0; kb4 < 4; ++kb4)
+                    s[kb4] -= dm;
             }
-            const float muse = m == kNegInf ? 0.f : m;
             // fp32 row sums (the LSE output keeps fp32 accuracy); the P V
             // product uses the probabilities rounded to bf16.
             bf16x8 pf[8];
@@ -281,7 +296,7 @@ void attn_fwd_bf16(AttnArgs a)
                 f32x8 pv;
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
-                    pv[x] = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + x], c2, -muse));
+                    pv[x] = __builtin_amdgcn_exp2f(s[t >> 1][8 * (t & 1) + x]);
                     ls[x & 1] += pv[x];
                 }
                 pf[t] = __builtin_convertvector(pv, bf16x8);

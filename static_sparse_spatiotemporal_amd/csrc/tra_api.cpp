@@ -554,9 +554,17 @@ tra_status tra_sparse_attn_fwd(const tra_tensor *Q, const tra_tensor *K, const t
     return hip_status(e);
 }
 
+size_t tra_sparse_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D)
+{
+    if (B < 0 || H < 0 || N < 0 || (D != 64 && D != 128))
+        return 0;
+    return tra::bwd_workspace(B, H, N, D).bytes;
+}
+
 tra_status tra_sparse_attn_bwd(const tra_tensor *Q, const tra_tensor *K, const tra_tensor *V, const tra_tensor *O,
                                const tra_tensor *dO, const float *LSE, const tra_mask *mask, tra_tensor *dQ,
-                               tra_tensor *dK, tra_tensor *dV, float *delta, float scale, void *hip_stream)
+                               tra_tensor *dK, tra_tensor *dV, void *workspace, size_t workspace_bytes, float scale,
+                               void *hip_stream)
 {
     const tra_tensor *ts[9] = {Q, K, V, O, dO, dQ, dK, dV, nullptr};
     for (int i = 0; i < 8; ++i)
@@ -569,7 +577,7 @@ tra_status tra_sparse_attn_bwd(const tra_tensor *Q, const tra_tensor *K, const t
         for (int i = 0; i < 8; ++i)
             if (!tensor_ok(ts[i]))
                 return TRA_ERR_INVALID;
-        if (LSE == nullptr || delta == nullptr)
+        if (LSE == nullptr || workspace == nullptr)
             return TRA_ERR_INVALID;
     }
     for (int i = 0; i < 8; ++i) {
@@ -607,6 +615,10 @@ tra_status tra_sparse_attn_bwd(const tra_tensor *Q, const tra_tensor *K, const t
     if (dev != mask->device)
         return TRA_ERR_INVALID;
 
+    const tra::BwdWorkspace ws = tra::bwd_workspace(Q->B, Q->H, Q->N, Q->D);
+    if (workspace_bytes < ws.bytes || ((uintptr_t)workspace) % 256 != 0)
+        return TRA_ERR_INVALID;
+
     tra::BwdArgs a;
     std::memset(&a, 0, sizeof(a));
     fill_attn_args(a.f, Q, K, V, nullptr, nullptr, mask, scale);
@@ -616,7 +628,9 @@ tra_status tra_sparse_attn_bwd(const tra_tensor *Q, const tra_tensor *K, const t
     a.dk = dK->data;
     a.dv = dV->data;
     a.lse = LSE;
-    a.delta = delta;
+    a.delta = (float *)((char *)workspace + ws.delta);
+    a.nlse2 = (float *)((char *)workspace + ws.nlse2);
+    a.qs = (char *)workspace + ws.qs;
     for (int i = 0; i < 3; ++i) {
         a.s_o[i] = O->stride[i];
         a.s_do[i] = dO->stride[i];

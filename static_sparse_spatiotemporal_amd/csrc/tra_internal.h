@@ -148,9 +148,17 @@ struct BwdArgs {
     const void *o, *dout;
     void *dq, *dk, *dv;
     const float *lse;
-    float *delta;
+    // workspace: delta = rowsum(dO o O), nlse2 = -LSE log2(e) (fp32 per row),
+    // qs = the queries times scale log2(e) rounded to bf16 ([B H N, D] rows)
+    float *delta, *nlse2;
+    void *qs;
     int64_t s_o[3], s_do[3], s_dq[3], s_dk[3], s_dv[3];
 };
+// Byte offsets of the backward workspace's parts (256-byte aligned) and its size.
+struct BwdWorkspace {
+    size_t delta, nlse2, qs, bytes;
+};
+BwdWorkspace bwd_workspace(int64_t B, int64_t H, int64_t N, int64_t D);
 hipError_t launch_attn_bwd_bf16(const BwdArgs &a, hipStream_t st);
 
 // SALAD linear branch (attn_linear_bf16.hip).

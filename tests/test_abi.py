@@ -127,8 +127,15 @@ def _tdesc(B=1, H=1, N=128, D=64, dtype=1, data=0x10000):
 def test_bwd_rejects_on_host(lib):
     t = _tdesc()
     r = ctypes.byref
-    assert lib.tra_sparse_attn_bwd(None, r(t), r(t), r(t), r(t), None, None, r(t), r(t), r(t), None, 0.0, None) == -1
-    assert lib.tra_sparse_attn_bwd(r(t), r(t), r(t), r(t), r(t), None, None, r(t), r(t), r(t), None, 0.0, None) == -1
+    assert lib.tra_sparse_attn_bwd(None, r(t), r(t), r(t), r(t), None, None, r(t), r(t), r(t), None, 0, 0.0,
+                                   None) == -1
+    assert lib.tra_sparse_attn_bwd(r(t), r(t), r(t), r(t), r(t), None, None, r(t), r(t), r(t), None, 0, 0.0,
+                                   None) == -1
+    # workspace size: two fp32 values and 2 D bytes per row, parts 256-byte aligned
+    assert lib.tra_sparse_attn_bwd_workspace_bytes(1, 2, 100, 128) == 1024 + 1024 + 51200
+    assert lib.tra_sparse_attn_bwd_workspace_bytes(1, 24, 131072, 128) == 24 * 131072 * (8 + 256)
+    assert lib.tra_sparse_attn_bwd_workspace_bytes(1, 1, 10, 96) == 0
+    assert lib.tra_sparse_attn_bwd_workspace_bytes(-1, 1, 10, 64) == 0
 
 
 def test_kvcache_rejects_on_host(lib):

@@ -2,7 +2,7 @@
 
 Tolerance: the gradients are accumulated in fp32 from bf16 inputs with the
 probabilities and dS rounded to bf16 for the MFMA products, and are returned
-in bf16, whose rounding alone is 2^-9 relative; every gradient element must
+in bf16, whose rounding alone is up to 2^-8 relative; every gradient element must
 lie within 2e-2 * max(1, max |reference|) of the oracle and the relative RMS
 error of each gradient must stay below 1e-2 (measured: 2.3e-3 to 2.5e-3).
 """
@@ -143,7 +143,8 @@ def test_bwd_headline_rows_and_identities(tra):
     sv = dv.double().sum(dim=2)
     so = do.double().sum(dim=2)
     sk = dk.double().sum(dim=2)
-    # bf16 rounding of each of the n gradient rows: |error| grows like sqrt(n) * 2^-9 * |row|
+    # bf16 rounding of each of the n gradient rows (RMS about 2^-9 of the value):
+    # |error| grows like sqrt(n) * 2^-9 * |row|
     lim = 4.0 * np.sqrt(w.n) * 2.0 ** -9 * float(dv.float().abs().max())
     print(f"       sum dV - sum dO: {float((sv - so).abs().max()):.3e}  sum dK: {float(sk.abs().max()):.3e}  limit {lim:.3e}",
           flush=True)

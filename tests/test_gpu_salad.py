@@ -4,7 +4,7 @@ Gate: fp32 sums of bf16 products, compared with the fp64 oracle within 1e-4
 (a mean of sigmoids, so values lie in (0, 1)); bitwise reproducible.
 Output: out = O_s + g (O_l W^T + bias), bf16 inputs, fp32 accumulation, bf16
 output: |out - ref| <= 1e-2 + 1e-2 |ref| per element and relative RMS <= 1e-2
-(bf16 output rounding is 2^-9 relative).
+(bf16 output rounding is at most 2^-8 relative).
 """
 import numpy as np
 import pytest

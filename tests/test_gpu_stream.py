@@ -3,7 +3,8 @@
 After appending frame i, attention for frame i's queries must equal the rows
 of frame i of the TRA_MASK_SWA_CAUSAL attention over frames 0 .. i (the ring
 keeps only the last `window` frames, which are exactly the frames those rows
-keep).  Same tolerances as the forward (bf16: 2e-2 on O, 1e-3 on LSE).
+keep).  Same tolerances as the forward (bf16: 2e-2 on O, the per-row bound
+of tests/tolerance.py on LSE).
 """
 import numpy as np
 import pytest
@@ -11,6 +12,7 @@ import torch
 
 import oracle
 import workloads
+from tests.tolerance import lse_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -49,12 +51,13 @@ def check_stream(tra, B, H, s, D, window, nframes, seed, check_frames=None, rows
         ref_o, ref_l = oracle.attention_rows(*arrs, spec, rows=rows)
         got_o = out[rows[:, 0], rows[:, 1], rows[:, 2] - i * s].float().cpu().numpy()
         got_l = lse[rows[:, 0], rows[:, 1], rows[:, 2] - i * s].cpu().numpy()
-        eo, el = float(np.abs(got_o - ref_o).max()), float(np.abs(got_l - ref_l).max())
-        print(f"         max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
+        dl = np.abs(got_l - ref_l)
+        eo, el = float(np.abs(got_o - ref_o).max()), float((dl / lse_bound(q[:, :, :n], k[:, :, :n], rows)).max())
+        print(f"         max|dO|={eo:.3e} max|dLSE|={float(dl.max()):.3e} (max/bound {el:.3f})", flush=True)
         errs.append((i, eo, el))
     cache.free()
     for i, eo, el in errs:
-        assert eo <= 2e-2 and el <= 1e-3, (i, eo, el)
+        assert eo <= 2e-2 and el <= 1, (i, eo, el)
 
 
 @pytest.mark.parametrize("D", [64, 128])
