@@ -320,12 +320,18 @@ void k_bwd_dkdv(BwdArgs a)
                 int ln = lane;
                 asm volatile("" : "+v"(ln));
                 const TileOffsets<D> off(ln);
+                // every lane-dependent value of the chunk comes from the
+                // opaque lane id too: held across the loop instead, such
+                // values were spilled and reloaded after the next tile's
+                // copies had been issued, and waiting for a reload then
+                // waited for those copies
+                const int lqc = ln & 31, hhc = ln >> 5;
                 // ---- S = Qs K^T - LSE log2 e, dP = dO V^T (32 queries x 32 keys) ----
                 // element i of this lane is query 32 c + 8 (i / 4) + 4 hh + i % 4
                 f32x16 s0;
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    const f32x4 nl = *(const f32x4 LDS_AS *)(tL + c * 32 + 8 * r4 + 4 * hh);
+                    const f32x4 nl = *(const f32x4 LDS_AS *)(tL + c * 32 + 8 * r4 + 4 * hhc);
 #pragma unroll
                     for (int x = 0; x < 4; ++x)
                         s0[4 * r4 + x] = nl[x];
@@ -346,22 +352,22 @@ void k_bwd_dkdv(BwdArgs a)
                     const uint32_t *mrow = mbase + ((size_t)em * kBlock + c * 32) * 4 + w4;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const int qi = 8 * (i >> 2) + 4 * hh + (i & 3);
-                        if (!((mrow[qi * 4] >> lq) & 1u))
+                        const int qi = 8 * (i >> 2) + 4 * hhc + (i & 3);
+                        if (!((mrow[qi * 4] >> lqc) & 1u))
                             s[i] = kNegInf;
                     }
                 }
                 if (rows_left < kBlock) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
-                        if (c * 32 + 8 * (i >> 2) + 4 * hh + (i & 3) >= rows_left)
+                        if (c * 32 + 8 * (i >> 2) + 4 * hhc + (i & 3) >= rows_left)
                             s[i] = kNegInf;
                 }
                 // four elements (one delta vector) at a time
                 bf16x4 pq[4], sq[4];
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    const f32x4 dl = *(const f32x4 LDS_AS *)(tD + c * 32 + 8 * r4 + 4 * hh);
+                    const f32x4 dl = *(const f32x4 LDS_AS *)(tD + c * 32 + 8 * r4 + 4 * hhc);
                     f32x4 pv, dsv;
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {

@@ -190,4 +190,18 @@ def test_bwd_errors(tra):
     with pytest.raises(tra.TraError) as e:
         tra.sparse_attn_bwd(q, k, v, out, lse, out, mask)
     assert e.value.status == -2  # fp32 backward is not provided
+    # bf16: a workspace one byte short, or off 256-byte alignment, is refused
+    qb, kb, vb = (x.to(torch.bfloat16) for x in (q, k, v))
+    ob, lb = tra.sparse_attn_fwd(qb, kb, vb, mask)
+    need = tra.sparse_attn_bwd_workspace_bytes(*qb.shape)
+    assert need == 2 * 256 * ((4 * w.n + 255) // 256) + 2 * w.n * w.D
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    for bad in (ws[:need - 1], ws[16:16 + need]):
+        with pytest.raises(tra.TraError) as e:
+            tra.sparse_attn_bwd(qb, kb, vb, ob, lb, ob, mask, workspace=bad)
+        assert e.value.status == -1
+    g1 = tra.sparse_attn_bwd(qb, kb, vb, ob, lb, ob, mask, workspace=ws[:need])
+    g2 = tra.sparse_attn_bwd(qb, kb, vb, ob, lb, ob, mask)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
     mask.free()
