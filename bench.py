@@ -202,6 +202,15 @@ def main():
     }
     mask.free()
 
+    if w.dtype == "bf16":
+        # measured peak: register-only MFMA loop, one workgroup of two waves
+        # per SIMD on every compute unit (about 80 ms, after a short warm-up)
+        tra.probe_mfma_peak(20000, stream=stream)
+        loop_ms, loop_flops = tra.probe_mfma_peak(600000, stream=stream)
+        loop_tflops = loop_flops / (loop_ms * 1e-3) / 1e12
+        extra.update({"mfma_loop_tflops": round(loop_tflops, 1),
+                      "pct_mfma_loop": round(100 * achieved / loop_tflops, 2)})
+
     if not args.no_dense and w.kind != "dense" and name == workloads.HEADLINE:
         dmask = tra.build_mask(w.f, w.s, "dense", granularity="block_any")
         tra.sparse_attn_fwd(q, k, v, dmask, out=out, lse=lse, stream=stream)

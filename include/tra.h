@@ -368,6 +368,21 @@ int32_t tra_last_hip_error(void);
 /* Library version as 10000 * major + 100 * minor + patch. */
 int32_t tra_version(void);
 
+/*
+ * tra_probe_mfma_peak -- a measurement helper, not part of the attention
+ * path: `blocks` workgroups of 8 waves (two per SIMD) each run `iterations`
+ * rounds of 4 independent v_mfma_f32_32x32x16_bf16 on register operands, with
+ * no memory traffic in the loop; one float per workgroup is written to
+ * `out` (device float[blocks]) so that the loop is kept.  The caller times
+ * the launch on `hip_stream`; *flops receives the MFMA flops it executes
+ * (blocks x 8 x 4 x iterations x 32768).  With one workgroup per compute
+ * unit this gives the bf16 MFMA rate the chip sustains under full MFMA load,
+ * the measured peak beside the data-sheet one.  Asynchronous; allocates
+ * nothing.  Errors: TRA_ERR_INVALID (iterations < 1, blocks < 1, null out
+ * or flops), TRA_ERR_HIP.
+ */
+tra_status tra_probe_mfma_peak(int64_t iterations, int32_t blocks, float *out, int64_t *flops, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

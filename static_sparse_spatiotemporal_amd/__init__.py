@@ -22,7 +22,7 @@ import numpy as np
 import torch
 
 __all__ = ["build_mask", "sparse_attn_fwd", "sparse_attn_bwd", "sparse_attn_bwd_workspace_bytes", "linear_attn_fwd", "salad_gate", "salad_combine",
-           "KVCache", "Mask", "TraError", "library_path", "load_library",
+           "KVCache", "Mask", "TraError", "library_path", "load_library", "probe_mfma_peak",
            "KINDS", "GRANULARITIES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -133,6 +133,9 @@ def load_library():
     lib.tra_last_hip_error.restype = ctypes.c_int32
     lib.tra_version.argtypes = []
     lib.tra_version.restype = ctypes.c_int32
+    lib.tra_probe_mfma_peak.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p]
+    lib.tra_probe_mfma_peak.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -397,6 +400,24 @@ def salad_gate(x: torch.Tensor, w: torch.Tensor, bias: float = 0.0, gate: torch.
 
 def salad_gate_workspace_bytes(B: int, N: int) -> int:
     return int(load_library().tra_salad_gate_workspace_bytes(B, N))
+
+
+def probe_mfma_peak(iterations: int = 200000, blocks: int | None = None, stream=None) -> tuple[float, int]:
+    """Measured bf16 MFMA peak (see tra_probe_mfma_peak): runs the register-only
+    MFMA loop once per compute unit and returns (milliseconds, flops)."""
+    lib = load_library()
+    if blocks is None:
+        blocks = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    out = torch.empty(blocks, dtype=torch.float32, device="cuda")
+    flops = ctypes.c_int64(0)
+    st = torch.cuda.current_stream() if stream is None else stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    _check(lib.tra_probe_mfma_peak(int(iterations), int(blocks), ctypes.c_void_p(out.data_ptr()), ctypes.byref(flops),
+                                   _stream_handle(st)), "tra_probe_mfma_peak")
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1), int(flops.value)
 
 
 def salad_combine(o_sparse: torch.Tensor, o_lin: torch.Tensor, weight: torch.Tensor, gate: torch.Tensor,

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtra.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["tra_api.cpp", "mask_build.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip", "attn_linear_bf16.hip",
-           "salad_bf16.hip"]
+           "salad_bf16.hip", "probe.hip"]
 ARCH = os.environ.get("TRA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -7,6 +7,7 @@
 #include <numeric>
 #include <vector>
 
+#include "probe.h"
 #include "salad.h"
 #include "tra_internal.h"
 
@@ -227,6 +228,14 @@ const char *tra_status_string(tra_status s)
 int32_t tra_last_hip_error(void) { return g_last_hip_error; }
 
 int32_t tra_version(void) { return 100; /* 0.1.0 */ }
+
+tra_status tra_probe_mfma_peak(int64_t iterations, int32_t blocks, float *out, int64_t *flops, void *hip_stream)
+{
+    if (iterations < 1 || blocks < 1 || out == nullptr || flops == nullptr)
+        return TRA_ERR_INVALID;
+    *flops = tra::mfma_loop_flops(iterations, blocks);
+    return hip_status(tra::launch_mfma_loop(iterations, blocks, out, (hipStream_t)hip_stream));
+}
 
 tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_params *p,
                           void *hip_stream, tra_mask **out)

@@ -138,6 +138,15 @@ def test_bwd_rejects_on_host(lib):
     assert lib.tra_sparse_attn_bwd_workspace_bytes(-1, 1, 10, 64) == 0
 
 
+def test_probe_rejects_on_host(lib):
+    flops = ctypes.c_int64(0)
+    out = ctypes.c_void_p(16)
+    assert lib.tra_probe_mfma_peak(0, 1, out, ctypes.byref(flops), None) == -1
+    assert lib.tra_probe_mfma_peak(10, 0, out, ctypes.byref(flops), None) == -1
+    assert lib.tra_probe_mfma_peak(10, 1, None, ctypes.byref(flops), None) == -1
+    assert lib.tra_probe_mfma_peak(10, 1, out, None, None) == -1
+
+
 def test_kvcache_rejects_on_host(lib):
     out = ctypes.c_void_p(7)
     assert lib.tra_kvcache_create(1, 1, 128, 64, 4, 1, None) == -1

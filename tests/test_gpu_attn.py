@@ -267,3 +267,15 @@ def test_errors_are_reported(tra):
     with pytest.raises(tra.TraError, match="SHAPE"):
         tra.build_mask(8, 12, "radius3d", grid_h=3, grid_w=5)
     mask.free()
+
+
+def test_mfma_probe_is_plausible(tra):
+    """The measured-peak loop runs and lands between a third of the
+    data-sheet bf16 peak and the peak itself; its flop count follows the
+    documented formula."""
+    ms, flops = tra.probe_mfma_peak(20000, blocks=4)
+    assert flops == 4 * 8 * 4 * 20000 * 32768
+    ms, flops = tra.probe_mfma_peak(100000)
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(f"[probe] MFMA loop {tflops:.0f} TFLOP/s", flush=True)
+    assert 2516.6 / 3 < tflops <= 2516.6 * 1.001
