@@ -71,6 +71,29 @@ def test_stream_window_one(tra):
     check_stream(tra, B=1, H=3, s=256, D=64, window=1, nframes=3, seed=700)
 
 
+def test_stream_odd_query_blocks(tra):
+    """384 tokens per frame: three query blocks, so the second pair of query
+    blocks holds one block."""
+    check_stream(tra, B=1, H=2, s=384, D=128, window=2, nframes=4, seed=710)
+
+
+def test_stream_repeat_is_bitwise(tra):
+    """The splits are merged in a fixed order: calling again on the same frame
+    gives the same bits."""
+    B, H, s, D, W = 1, 8, 256, 64, 8
+    q, k, v = frames_qkv(B, H, W + 2, s, D, 720)
+    cache = tra.KVCache(B, H, s, D, W)
+    for i in range(W + 2):
+        sl = slice(i * s, (i + 1) * s)
+        cache.append(k[:, :, sl], v[:, :, sl])
+    sl = slice((W + 1) * s, (W + 2) * s)
+    outs = [cache.attn(q[:, :, sl]) for _ in range(4)]
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+    cache.free()
+
+
 def test_stream_workload_shape(tra):
     """The n = 16384 sliding-window workload's shape (16 heads, 256 tokens per
     frame, d = 64, window 16), streamed for 20 frames (the ring wraps at 16)."""
