@@ -279,3 +279,37 @@ def test_mfma_probe_is_plausible(tra):
     tflops = flops / (ms * 1e-3) / 1e12
     print(f"[probe] MFMA loop {tflops:.0f} TFLOP/s", flush=True)
     assert 2516.6 / 3 < tflops <= 2516.6 * 1.001
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [0.03, 0.2])
+def test_custom_scale(tra, dt, scale):
+    """A caller scale instead of 1/sqrt(d): the oracle with the same scale, and
+    (bf16) the LSE bound of the query rounding at that scale."""
+    w = workloads.Workload("radial_f6_s100", "radial", "element", 6, 100, 1, 2, 128, dt, seed=31 + int(100 * scale))
+    q, k, v = workloads.make_qkv(w, device="cuda")
+    mask = build(tra, w)
+    out, lse = tra.sparse_attn_fwd(q, k, v, mask, scale=scale)
+    torch.cuda.synchronize()
+    spec = spec_of(w)
+    ref_o, ref_l = oracle.attention_rows(*(workloads.to_oracle_array(x) for x in (q, k, v)), spec, scale=scale)
+    eo = float(np.abs(out.float().cpu().numpy().reshape(-1, w.D) - ref_o).max())
+    dl = np.abs(lse.cpu().numpy().reshape(-1) - ref_l)
+    ratio = float((dl / lse_bound(q, k, scale=scale)).max())
+    print(f"[scale] {dt} scale={scale}: max|dO|={eo:.3e} max|dLSE|={float(dl.max()):.3e} (max/bound {ratio:.3f})",
+          flush=True)
+    assert eo <= TOL_O[dt] and ratio <= 1
+    mask.free()
+
+
+def test_lse_output_is_optional(tra):
+    """Skipping the LSE output leaves O bit for bit unchanged."""
+    w = workloads.WORKLOADS["radial_f20_s1536_block"].replace(H=2)
+    q, k, v = workloads.make_qkv(w, device="cuda")
+    mask = build(tra, w)
+    o1, l1 = tra.sparse_attn_fwd(q, k, v, mask)
+    o2, l2 = tra.sparse_attn_fwd(q, k, v, mask, lse=False)
+    torch.cuda.synchronize()
+    assert l2 is None and l1 is not None
+    assert torch.equal(o1, o2)
+    mask.free()

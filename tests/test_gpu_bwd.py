@@ -205,3 +205,25 @@ def test_bwd_errors(tra):
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(g1, g2))
     mask.free()
+
+
+def test_bwd_custom_scale(tra):
+    """Gradients for a caller scale instead of 1/sqrt(d) (dQ = scale dS K,
+    dK = scale dS^T Q) against the oracle at that scale."""
+    scale = 0.05
+    w = workloads.Workload("radial_f6_s128", "radial", "element", 6, 128, 1, 2, 64, "bf16", seed=57)
+    mask = tra.build_mask(w.f, w.s, w.kind, **w.mask_kwargs())
+    q, k, v = workloads.make_qkv(w, device="cuda")
+    do = make_dout(w)
+    out, lse = tra.sparse_attn_fwd(q, k, v, mask, scale=scale)
+    dq, dk, dv = tra.sparse_attn_bwd(q, k, v, out, lse, do, mask, scale=scale)
+    torch.cuda.synchronize()
+    mask.free()
+    arrs = [workloads.to_oracle_array(x) for x in (q, k, v, do)]
+    refs = oracle.attention_bwd_rows(*arrs, spec_of(w), scale=scale)
+    for name, got, ref in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs):
+        g = got.float().cpu().numpy().reshape(-1, w.D)
+        e = float(np.abs(g - ref).max())
+        rel = float(np.sqrt(((g - ref) ** 2).sum() / max((ref ** 2).sum(), 1e-30)))
+        print(f"[bwd scale] {name}: max|err|={e:.3e} rel-rms={rel:.2e}", flush=True)
+        assert e <= tol(ref) and rel <= 1e-2, (name, e, rel)
