@@ -313,3 +313,25 @@ def test_lse_output_is_optional(tra):
     assert l2 is None and l1 is not None
     assert torch.equal(o1, o2)
     mask.free()
+
+
+def test_mask_serves_other_batch_and_head_counts(tra):
+    """The mask is shared by every (b, h) and the work queue is sized per call:
+    one mask serves B=1, H=3 and then B=2, H=5 (sampled rows vs the oracle,
+    and the first call repeated bit for bit afterwards)."""
+    base = workloads.WORKLOADS["radial_f20_s1536_block"]
+    mask = build(tra, base)
+    first = None
+    for B, H in ((1, 3), (2, 5)):
+        w = base.replace(B=B, H=H)
+        q, k, v = workloads.make_qkv(w, device="cuda")
+        rows = expected.sample_rows(w.n, w.B, w.H, heads_per_batch=2, blocks=2, seed=B * 10 + H)
+        eo, el, out, _ = run_and_compare(tra, w, q, k, v, rows=rows, mask=mask, tag=f" (B={B} H={H})")
+        assert eo <= TOL_O["bf16"] and el <= 1
+        if first is None:
+            first = (q, k, v, out.clone())
+    q, k, v, out1 = first
+    again, _ = tra.sparse_attn_fwd(q, k, v, mask)
+    torch.cuda.synchronize()
+    assert torch.equal(again, out1)
+    mask.free()
