@@ -14,6 +14,8 @@ Definitions followed (pages on the method; see ``oracle.h`` for detail):
     dilation, or eq. 4 on block indices as a second reading)
   * Radial Attention, section 4 -- the "sink" of the complexity count, as
     key frames every query keeps (sink_frames)
+  * SALAD, sections 2.1-2.2 -- the ReLU-kernel linear-attention branch, the
+    scalar sigmoid gate and the gated, projected sum of the two branches
 
 The C part (``oracle.c``) does the arithmetic; this module only marshals numpy
 arrays through ctypes.
