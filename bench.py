@@ -120,6 +120,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the measured-MFMA-peak loop (for profiled runs)")
     ap.add_argument("--cpu-seconds", type=float, default=30.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 2 GiB device copy (counter calibration)")
@@ -202,7 +204,7 @@ def main():
     }
     mask.free()
 
-    if w.dtype == "bf16":
+    if w.dtype == "bf16" and not args.no_probe:
         # measured peak: register-only MFMA loop, one workgroup of two waves
         # per SIMD on every compute unit (about 80 ms, after a short warm-up)
         tra.probe_mfma_peak(20000, stream=stream)

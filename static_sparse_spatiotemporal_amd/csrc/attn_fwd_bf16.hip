@@ -407,7 +407,10 @@ __global__ __launch_bounds__(256) void k_merge_splits(AttnArgs a)
     const int part = threadIdx.x & 7;
     if (r >= rows)
         return;
+    // both split loops are unrolled so that the loads of several splits are
+    // in flight together (the merge is latency-bound)
     float mx = kNegInf;
+#pragma unroll 8
     for (int x = 0; x < a.nsplit; ++x)
         mx = fmaxf(mx, a.part_lse[(int64_t)x * rows + r]);
     float acc[PER];
@@ -415,6 +418,7 @@ __global__ __launch_bounds__(256) void k_merge_splits(AttnArgs a)
     for (int e = 0; e < PER; ++e)
         acc[e] = 0.f;
     float tot = 0.f;
+#pragma unroll 4
     for (int x = 0; x < a.nsplit; ++x) {
         const float w = __builtin_amdgcn_exp2f(a.part_lse[(int64_t)x * rows + r] - mx);
         tot += w;
