@@ -346,10 +346,13 @@ void k_bwd_dkdv(BwdArgs a)
                 }
                 if (em >= 0) {
                     // base taken opaque in scalar registers here: hoisted, it
-                    // was held in (spilled) vector registers across the loop
-                    const uint32_t *mbase = a.f.mask.emask;
+                    // was held in (spilled) vector registers across the loop.
+                    // A global (not generic) pointer: generic loads may alias
+                    // LDS and were issued one at a time, each behind a wait.
+                    typedef const __attribute__((address_space(1))) uint32_t gu32;
+                    gu32 *mbase = (gu32 *)a.f.mask.emask;
                     asm volatile("" : "+s"(mbase));
-                    const uint32_t *mrow = mbase + ((size_t)em * kBlock + c * 32) * 4 + w4;
+                    gu32 *mrow = mbase + ((size_t)em * kBlock + c * 32) * 4 + w4;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int qi = 8 * (i >> 2) + 4 * hhc + (i & 3);
