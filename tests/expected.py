@@ -55,6 +55,41 @@ def csr(cls: np.ndarray):
     return row_ptr, np.array(cols, dtype=np.int32), np.array(eidx, dtype=np.int32)
 
 
+def pair_schedule(keep: np.ndarray, s: int):
+    """(items, tile loads) of the library's pair schedule over the rows of
+    the boolean block matrix `keep`, by its stated rule: rows are taken in
+    order; an unpaired row r takes, among the unpaired rows r + 1 and
+    r + s / 128 (the latter when s is a multiple of 128 above 128), the one
+    whose kept-block set has the larger Jaccard overlap with r's, the first
+    on ties, if that overlap exceeds 1/2 (two empty sets count as 1).  A pair
+    loads the union of its two rows' blocks."""
+    nr = keep.shape[0]
+    offs = [1] + ([s // BLOCK] if s % BLOCK == 0 and s // BLOCK > 1 else [])
+    used = np.zeros(nr, dtype=bool)
+    items, loads = 0, 0
+    for r in range(nr):
+        if used[r]:
+            continue
+        best, bj = -1, 0.5
+        for off in offs:
+            r2 = r + off
+            if r2 >= nr or used[r2]:
+                continue
+            inter = int((keep[r] & keep[r2]).sum())
+            uni = int((keep[r] | keep[r2]).sum())
+            j = inter / uni if uni else 1.0
+            if j > bj:
+                bj, best = j, r2
+        used[r] = True
+        items += 1
+        if best >= 0:
+            used[best] = True
+            loads += int((keep[r] | keep[best]).sum())
+        else:
+            loads += int(keep[r].sum())
+    return items, loads
+
+
 def bitmap(cls: np.ndarray):
     nb = cls.shape[0]
     words = (nb + 31) // 32

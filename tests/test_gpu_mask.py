@@ -89,6 +89,11 @@ def check_mask(spec: oracle.MaskSpec, counts=None):
     else:
         assert info["kept_elems"] == int(expected.kept_keys_per_row(spec, cls).sum())
     assert info["min_row_blocks"] == per_row.min() and info["max_row_blocks"] == per_row.max()
+    # the kernels' pair schedules, over query blocks (forward, dQ) and over
+    # key blocks (dK/dV), against their rule restated on the block classes
+    keep = cls > 0
+    assert (info["work_items"], info["tile_loads"]) == expected.pair_schedule(keep, spec.s)
+    assert (info["bwd_work_items"], info["bwd_tile_loads"]) == expected.pair_schedule(keep.T, spec.s)
     m.free()
     return counts, cls
 
