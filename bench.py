@@ -42,6 +42,18 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name, as the kernel reports it (empty if unknown)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch of the attention kernel from the committed rocprofv3
     counter summary, if it was taken on the current kernel source."""
@@ -191,6 +203,9 @@ def main():
                  + 8 * info["kept_blocks"] + 2048 * info["partial_blocks"])
 
     extra = {
+        "seed": w.seed,
+        "torch": torch.__version__,
+        "host_cpu": host_cpu_model(),
         "mask_build_ms": round(build_ms, 3),
         "launch_ms_mean": round(launch_ms, 4),
         "launch_ms_median": round(float(np.median(ev_ms)), 4),
