@@ -25,7 +25,7 @@
 // global_load_lds_dwordx4 into double buffers (one LDS array each, named
 // statically in every step), XOR-swizzled so that both the row reads
 // (ds_read_b128) and the transposed reads (ds_read_b64_tr_b16) of one tile
-// stay spread over the banks.
+// are free of bank conflicts (see swz).
 #include "attn_common.h"
 
 namespace tra {
@@ -49,10 +49,22 @@ struct Geo {
 };
 
 // Physical 16-byte chunk of logical chunk c in row `row`: c ^ swz(row).
+// Every streamed tile is read both ways, so one swizzle serves both (64
+// banks of 4 bytes; a row is 64 banks at D = 128, 32 at D = 64):
+//   - row reads (ds_read_b128): 16 lanes read rows r .. r + 15 at one
+//     logical chunk, so swz must differ over those rows (at D = 64: over
+//     the rows of one parity, as two rows share a bank line);
+//   - transposed reads (ds_read_b64_tr_b16): 32 lanes read 4 rows 4k ..
+//     4k + 3 at the 4 chunks of one aligned group, so swz must move those
+//     rows (at D = 64: the two rows of each parity) into different groups,
+//     i.e. differ in bits 2-3 (bit 2).
+// Both hold for the low row bits rotated: (r & 3) << 2 | (r >> 2) & 3, and
+// at D = 64 ((r >> 1) & 1) << 2 | (r >> 2) & 3.  (Plain r & 15 leaves the
+// 4 rows of a transposed read in one group: 4-way conflicts.)
 template <int D>
 __device__ inline int swz(int row)
 {
-    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+    return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 
 __device__ inline void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
