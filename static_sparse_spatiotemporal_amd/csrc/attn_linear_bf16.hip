@@ -40,10 +40,17 @@ struct LGeo {
     static constexpr int NDB = D / 32;
 };
 
+// Physical 16-byte chunk of logical chunk c in row `row`: c ^ lswz(row).
+// The reduce kernel reads its tiles transposed (32 lanes over 4 rows 4k ..
+// 4k + 3 at the 4 chunks of one aligned group), the apply kernel reads
+// KV^T by rows (16 lanes over 16 rows at one chunk).  Rotating the low row
+// bits keeps both free of bank conflicts (64 banks of 4 bytes): the 16 rows
+// get distinct chunks and the 4 rows distinct chunk groups (at D = 64,
+// where two rows share a bank line, within each row parity).
 template <int D>
 __device__ inline int lswz(int row)
 {
-    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+    return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 
 // Copy a kLinRows-row tile (rows row0 .., clamped to N - 1) of X into LDS.
