@@ -133,7 +133,11 @@ struct CombineArgs {
 };
 
 // Physical 16-byte chunk of logical chunk c in LDS row `row` (8 per row).
-__device__ inline int cswz(int row) { return row & 7; }
+// A 128-byte row is half of the 64 banks, so rows r and r + 1 share a bank
+// line; the 16 rows of one ds_read_b128 pass then need distinct chunks
+// within each row parity, which (r >> 1) & 7 gives (r & 7 repeats at r + 8:
+// 2-way conflicts).
+__device__ inline int cswz(int row) { return (row >> 1) & 7; }
 
 __device__ inline void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
