@@ -49,11 +49,15 @@ struct GateArgs {
 
 __global__ __launch_bounds__(kGateThreads) void k_salad_gate_part(GateArgs a)
 {
-    extern __shared__ float sW[];  // C floats
+    // w stays bf16 in LDS: a lane's 8 values are then 16 contiguous bytes
+    // (one ds_read_b128, 16 lanes covering the 64 banks once), and each
+    // pair of products goes through one bf16 dot instruction (products of
+    // bf16 values are exact in fp32).
+    extern __shared__ __attribute__((aligned(16))) __bf16 sW[];  // C values
     __shared__ float sSum[kGateThreads / 64];
     const int b = blockIdx.y, part = blockIdx.x;
     for (int c = threadIdx.x; c < a.C; c += kGateThreads)
-        sW[c] = (float)a.w[c];
+        sW[c] = a.w[c];
     __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t n0 = (int64_t)part * a.rows_per_part;
@@ -63,10 +67,13 @@ __global__ __launch_bounds__(kGateThreads) void k_salad_gate_part(GateArgs a)
         const __bf16 *row = a.x + b * a.sxb + n * a.sxn;
         float z = 0.f;
         for (int c = lane * 8; c < a.C; c += 512) {
-            const bf16x8 v = *(const bf16x8 *)(row + c);
+            const uint4 v = *(const uint4 *)(row + c);
+            const uint4 wv = *(const uint4 *)(sW + c);
+            const uint32_t vs[4] = {v.x, v.y, v.z, v.w}, ws[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                z = fmaf((float)v[j], sW[c + j], z);
+            for (int j = 0; j < 4; ++j)
+                z = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, vs[j]), __builtin_bit_cast(bf16x2, ws[j]),
+                                                    z, false);
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1)
@@ -342,7 +349,7 @@ hipError_t launch_salad_gate(const void *x, const int64_t sx[2], const void *w, 
     a.part = (float *)workspace;
     a.gate = gate;
     hipLaunchKernelGGL(k_salad_gate_part, dim3((unsigned)a.parts, (unsigned)B), dim3(kGateThreads),
-                       (size_t)C * sizeof(float), stream, a);
+                       (size_t)C * sizeof(__bf16), stream, a);
     hipLaunchKernelGGL(k_salad_gate_final, dim3((unsigned)B), dim3(64), 0, stream, a);
     return hipGetLastError();
 }
