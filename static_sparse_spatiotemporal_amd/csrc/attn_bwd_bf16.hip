@@ -112,27 +112,28 @@ __device__ inline void copy_row_vec(const float *x, int row0, int N, float LDS_A
 //             half), columns 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4).
 template <int D>
 struct TileOffsets {
-    int row[Geo<D>::NKS];
-    int tr[Geo<D>::NDB][2];
+    // With XOR swizzles of the low row bits, the fragment of k-step ks is
+    // row0 ^ (ks << 5) and that of 32-row block db is tr0[x] ^ (db << 6)
+    // (the XOR touches only bits below the row pitch), so three values per
+    // lane stand for all of them.
+    int row0;
+    int tr0[2];
     __device__ TileOffsets(int lane)
     {
         using G = Geo<D>;
         const int lq = lane & 31, hh = lane >> 5;
-#pragma unroll
-        for (int ks = 0; ks < G::NKS; ++ks)
-            row[ks] = lq * G::ROWB + (((2 * ks + hh) ^ swz<D>(lq)) << 4);
+        row0 = lq * G::ROWB + ((hh ^ swz<D>(lq)) << 4);
         const int g = lane >> 4, r16 = lane & 15;
         const int ra = 4 * hh + (r16 >> 2);
+        const int d = (g & 1) * 16 + 4 * (r16 & 3);
 #pragma unroll
-        for (int db = 0; db < G::NDB; ++db) {
-            const int d = db * 32 + (g & 1) * 16 + 4 * (r16 & 3);
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int r = ra + 8 * x;
-                tr[db][x] = r * G::ROWB + (((d >> 3) ^ swz<D>(r)) << 4) + ((d & 7) << 1);
-            }
+        for (int x = 0; x < 2; ++x) {
+            const int r = ra + 8 * x;
+            tr0[x] = r * G::ROWB + (((d >> 3) ^ swz<D>(r)) << 4) + ((d & 7) << 1);
         }
     }
+    __device__ int row(int ks) const { return row0 ^ (ks << 5); }
+    __device__ int tr(int db, int x) const { return tr0[x] ^ (db << 6); }
 };
 
 // A operand (32 columns of block db x 16 rows 16 t ..) by transposed reads;
@@ -141,8 +142,8 @@ template <int D>
 __device__ inline bf16x8 read_tr(const char LDS_AS *tile, const TileOffsets<D> &off, int t, int db)
 {
     const char LDS_AS *p = tile + t * 16 * Geo<D>::ROWB;
-    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(p + off.tr[db][0]));
-    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(p + off.tr[db][1]));
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(p + off.tr(db, 0)));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(p + off.tr(db, 1)));
     return __builtin_shufflevector(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b), 0, 1, 2, 3, 4,
                                    5, 6, 7);
 }
@@ -326,9 +327,9 @@ void k_bwd_dkdv(BwdArgs a)
 #pragma unroll 1
             for (int c = 0; c < 4; ++c) {
                 const int cr = c * 32 * G::ROWB;
-                // fragment offsets are recomputed per chunk (a few VALU
-                // operations) instead of held in 16 registers across the
-                // loop; recomputing them at every use instead costs 25%
+                // the fragment base offsets are recomputed per chunk (a few
+                // VALU operations) instead of held in registers across the
+                // loop
                 int ln = lane;
                 asm volatile("" : "+v"(ln));
                 const TileOffsets<D> off(ln);
@@ -351,8 +352,8 @@ void k_bwd_dkdv(BwdArgs a)
                 f32x16 s, dp = f32x16{};
 #pragma unroll
                 for (int ks = 0; ks < G::NKS; ++ks) {
-                    const bf16x8 qa = *(const bf16x8 LDS_AS *)(tQ + cr + off.row[ks]);
-                    const bf16x8 ga = *(const bf16x8 LDS_AS *)(tO + cr + off.row[ks]);
+                    const bf16x8 qa = *(const bf16x8 LDS_AS *)(tQ + cr + off.row(ks));
+                    const bf16x8 ga = *(const bf16x8 LDS_AS *)(tO + cr + off.row(ks));
                     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], ks == 0 ? s0 : s, 0, 0, 0);
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
                 }
@@ -546,7 +547,7 @@ void k_bwd_dq(BwdArgs a)
                 for (int ks = 0; ks < G::NKS; ++ks)
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb) {
-                        const int ro = (2 * hf + kb) * 32 * G::ROWB + off.row[ks];
+                        const int ro = (2 * hf + kb) * 32 * G::ROWB + off.row(ks);
                         const bf16x8 ka = *(const bf16x8 LDS_AS *)(tK + ro);
                         const bf16x8 va = *(const bf16x8 LDS_AS *)(tV + ro);
                         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? s0 : s[kb], 0, 0, 0);
