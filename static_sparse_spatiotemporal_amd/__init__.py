@@ -151,6 +151,87 @@ def _stream_handle(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(int(stream.cuda_stream))
 
 
+# ---- argument checks -------------------------------------------------------
+# The C ABI takes raw device pointers and cannot tell a host pointer, a tensor
+# of the wrong dtype or one that is too small from a good one: every tensor is
+# checked here, before anything is handed to the library.
+
+def _fail(msg: str):
+    raise ValueError(msg)
+
+
+def _need_tensor(name: str, t, device: torch.device | None, dtype=None, shape=None, contiguous: bool = False):
+    """`t` is a tensor on `device` (the call's device: that of its first
+    tensor; None for that first tensor itself, which must be on a HIP
+    device), of `dtype` (one dtype or a tuple), of `shape` when given, and
+    contiguous when asked."""
+    if not isinstance(t, torch.Tensor):
+        _fail(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if device is None:
+        if not t.is_cuda:
+            _fail(f"{name} must be on a HIP device (got {t.device})")
+    elif t.device != device:
+        _fail(f"{name} is on {t.device}, the call runs on {device}")
+    if dtype is not None:
+        ok = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in ok:
+            _fail(f"{name} must have dtype {' or '.join(str(d) for d in ok)}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        _fail(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        _fail(f"{name} must be contiguous")
+    return t
+
+
+def _need_bhnd(name: str, t, device: torch.device | None, dtype=None, shape=None):
+    """A [B, H, N, D] view the kernels can read: unit stride in D, the other
+    strides non-negative multiples of 16 bytes, data 16-byte aligned."""
+    _need_tensor(name, t, device, dtype=dtype, shape=shape)
+    if t.dim() != 4:
+        _fail(f"{name} must be a [B, H, N, D] tensor, got {t.dim()} dims")
+    if t.numel() == 0:
+        return t
+    vec = 16 // t.element_size()
+    st = t.stride()
+    if st[3] != 1 and t.shape[3] > 1:
+        _fail(f"{name} must have unit stride in its last dimension")
+    if any(x < 0 or x % vec for x in st[:3]):
+        _fail(f"{name}: strides {tuple(st[:3])} must be multiples of {vec} elements (16 bytes)")
+    if t.data_ptr() % 16:
+        _fail(f"{name} data must be 16-byte aligned")
+    return t
+
+
+def _need_workspace(name: str, t, device: torch.device, need: int):
+    _need_tensor(name, t, device, dtype=torch.uint8, contiguous=True)
+    if t.numel() < need:
+        _fail(f"{name} holds {t.numel()} bytes, the call needs {need}")
+    if t.data_ptr() % 256:
+        _fail(f"{name} must be 256-byte aligned")
+    return t
+
+
+def _call_stream(stream, device: torch.device):
+    """The torch stream the call runs on (the device's current stream by
+    default); it must belong to the tensors' device."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if not isinstance(stream, torch.cuda.Stream):
+        _fail(f"stream must be a torch.cuda.Stream, got {type(stream).__name__}")
+    if stream.device != device:
+        _fail(f"stream is on {stream.device}, the tensors on {device}")
+    return stream
+
+
+def _new(shape, dtype, device, stream):
+    """A tensor allocated for use on `stream`: the caching allocator hands its
+    block out again only in that stream's order, so a default buffer that is
+    dropped when the call returns cannot be reused while the call's kernels
+    still read or write it."""
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 class Mask:
     """A compiled static mask (owns device memory until freed)."""
 
@@ -219,7 +300,7 @@ def _desc(t: torch.Tensor) -> TensorDesc:
     elif t.dtype == torch.float32:
         dt = _F32
     else:
-        raise TypeError(f"unsupported dtype {t.dtype}")
+        raise ValueError(f"unsupported dtype {t.dtype}")
     d = TensorDesc()
     d.data = t.data_ptr()
     d.dtype = dt
@@ -229,31 +310,44 @@ def _desc(t: torch.Tensor) -> TensorDesc:
     return d
 
 
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr() if t is not None else None)
+
+
+def _lse_arg(lse, q: torch.Tensor, stream):
+    """`lse` = True: a new [B, H, n] fp32 tensor; a tensor: checked and written
+    in place; False/None: not computed."""
+    if lse is True:
+        return _new(q.shape[:3], torch.float32, q.device, stream)
+    if lse is False or lse is None:
+        return None
+    return _need_tensor("lse", lse, q.device, dtype=torch.float32, shape=q.shape[:3], contiguous=True)
+
+
 def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
                     out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True,
                     scale: float | None = None, stream=None):
     """O = softmax((Q K^T + M) * scale) V on the GPU (see tra_sparse_attn_fwd).
 
-    q, k, v: [B, H, n, D] cuda tensors (bf16 or fp32).  `out` defaults to a new
-    contiguous tensor; `lse` = True allocates a [B, H, n] fp32 tensor, a tensor
-    is written in place, False/None skips it.  Returns (out, lse or None).
+    q, k, v: [B, H, n, D] cuda tensors (bf16 or fp32, one dtype) on one
+    device.  `out` defaults to a new contiguous tensor; `lse` = True allocates
+    a [B, H, n] fp32 tensor, a tensor is written in place, False/None skips
+    it.  Returns (out, lse or None).
     """
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
-        raise ValueError("q, k, v must be on a HIP device")
+    _need_bhnd("q", q, None, dtype=(torch.bfloat16, torch.float32))
+    dev = q.device
+    _need_bhnd("k", k, dev, dtype=q.dtype, shape=q.shape)
+    _need_bhnd("v", v, dev, dtype=q.dtype, shape=q.shape)
+    st = _call_stream(stream, dev)
     if out is None:
-        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
-    if lse is True:
-        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    elif lse is False:
-        lse = None
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
-                            or tuple(lse.shape) != tuple(q.shape[:3])):
-        raise ValueError("lse must be a contiguous float32 [B, H, n] tensor")
+        out = _new(q.shape, q.dtype, dev, st)
+    _need_bhnd("out", out, dev, dtype=q.dtype, shape=q.shape)
+    lse = _lse_arg(lse, q, st)
     dq, dk, dv, do = _desc(q), _desc(k), _desc(v), _desc(out)
-    _check(load_library().tra_sparse_attn_fwd(
-        ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), mask.handle, ctypes.byref(do),
-        ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
-        float(scale) if scale else 0.0, _stream_handle(stream)), "tra_sparse_attn_fwd")
+    with torch.cuda.device(dev):
+        _check(load_library().tra_sparse_attn_fwd(
+            ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), mask.handle, ctypes.byref(do),
+            _ptr(lse), float(scale) if scale else 0.0, _stream_handle(st)), "tra_sparse_attn_fwd")
     return out, lse
 
 
@@ -268,20 +362,30 @@ def sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     sparse_attn_bwd_workspace_bytes bytes (default: new).
     """
     lib = load_library()
+    _need_bhnd("q", q, None, dtype=torch.bfloat16)
+    dev = q.device
     B, H, n, D = q.shape
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _need_bhnd(name, t, dev, dtype=torch.bfloat16, shape=q.shape)
+    _need_tensor("lse", lse, dev, dtype=torch.float32, shape=q.shape[:3], contiguous=True)
+    st = _call_stream(stream, dev)
     if grads is None:
-        grads = tuple(torch.empty(q.shape, dtype=q.dtype, device=q.device) for _ in range(3))
+        grads = tuple(_new(q.shape, q.dtype, dev, st) for _ in range(3))
+    if len(grads) != 3:
+        _fail("grads must be (dq, dk, dv)")
+    for name, t in zip(("dq", "dk", "dv"), grads):
+        _need_bhnd(name, t, dev, dtype=torch.bfloat16, shape=q.shape)
+    need = int(lib.tra_sparse_attn_bwd_workspace_bytes(B, H, n, D))
     if workspace is None:
-        workspace = torch.empty(int(lib.tra_sparse_attn_bwd_workspace_bytes(B, H, n, D)), dtype=torch.uint8,
-                                device=q.device)
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
-        raise ValueError("lse must be a contiguous float32 [B, H, n] tensor")
+        workspace = _new(max(need, 1), torch.uint8, dev, st)
+    _need_workspace("workspace", workspace, dev, need)
     descs = [_desc(t) for t in (q, k, v, out, dout)]
     gd = [_desc(t) for t in grads]
-    _check(lib.tra_sparse_attn_bwd(
-        *(ctypes.byref(d) for d in descs), ctypes.c_void_p(lse.data_ptr()), mask.handle,
-        *(ctypes.byref(d) for d in gd), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
-        float(scale) if scale else 0.0, _stream_handle(stream)), "tra_sparse_attn_bwd")
+    with torch.cuda.device(dev):
+        _check(lib.tra_sparse_attn_bwd(
+            *(ctypes.byref(d) for d in descs), _ptr(lse), mask.handle,
+            *(ctypes.byref(d) for d in gd), _ptr(workspace), workspace.numel(),
+            float(scale) if scale else 0.0, _stream_handle(st)), "tra_sparse_attn_bwd")
     return grads
 
 
@@ -301,6 +405,7 @@ class KVCache:
         self._h = h
         self.shape = (B, H, s, D)
         self.window = window
+        self.device = torch.device("cuda", torch.cuda.current_device())
 
     @property
     def handle(self):
@@ -309,23 +414,27 @@ class KVCache:
         return self._h
 
     def append(self, k: torch.Tensor, v: torch.Tensor, stream=None):
+        _need_bhnd("k", k, self.device, dtype=torch.bfloat16, shape=self.shape)
+        _need_bhnd("v", v, self.device, dtype=torch.bfloat16, shape=self.shape)
+        st = _call_stream(stream, self.device)
         dk, dv = _desc(k), _desc(v)
-        _check(load_library().tra_kvcache_append(self.handle, ctypes.byref(dk), ctypes.byref(dv),
-                                                 _stream_handle(stream)), "tra_kvcache_append")
+        with torch.cuda.device(self.device):
+            _check(load_library().tra_kvcache_append(self.handle, ctypes.byref(dk), ctypes.byref(dv),
+                                                     _stream_handle(st)), "tra_kvcache_append")
 
     def attn(self, q: torch.Tensor, out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True,
              scale: float | None = None, stream=None):
+        _need_bhnd("q", q, self.device, dtype=torch.bfloat16, shape=self.shape)
+        st = _call_stream(stream, self.device)
         if out is None:
-            out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
-        if lse is True:
-            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-        elif lse is False:
-            lse = None
+            out = _new(q.shape, q.dtype, q.device, st)
+        _need_bhnd("out", out, self.device, dtype=torch.bfloat16, shape=self.shape)
+        lse = _lse_arg(lse, q, st)
         dq, do = _desc(q), _desc(out)
-        _check(load_library().tra_kvcache_attn(
-            self.handle, ctypes.byref(dq), ctypes.byref(do),
-            ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
-            float(scale) if scale else 0.0, _stream_handle(stream)), "tra_kvcache_attn")
+        with torch.cuda.device(self.device):
+            _check(load_library().tra_kvcache_attn(
+                self.handle, ctypes.byref(dq), ctypes.byref(do), _ptr(lse),
+                float(scale) if scale else 0.0, _stream_handle(st)), "tra_kvcache_attn")
         return out, lse
 
     def frames(self):
@@ -357,21 +466,40 @@ def linear_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     at least linear_attn_workspace_bytes bytes) defaults to a new one.
     """
     lib = load_library()
+    _need_bhnd("q", q, None, dtype=torch.bfloat16)
+    dev = q.device
+    _need_bhnd("k", k, dev, dtype=torch.bfloat16, shape=q.shape)
+    _need_bhnd("v", v, dev, dtype=torch.bfloat16, shape=q.shape)
     B, H, n, D = q.shape
+    st = _call_stream(stream, dev)
     need = int(lib.tra_linear_attn_workspace_bytes(B, H, n, D))
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _new(max(need, 1), torch.uint8, dev, st)
+    _need_workspace("workspace", workspace, dev, need)
     if out is None:
-        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+        out = _new(q.shape, q.dtype, dev, st)
+    _need_bhnd("out", out, dev, dtype=torch.bfloat16, shape=q.shape)
     descs = [_desc(t) for t in (q, k, v, out)]
-    _check(lib.tra_linear_attn_fwd(*(ctypes.byref(d) for d in descs), float(eps),
-                                   ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
-                                   _stream_handle(stream)), "tra_linear_attn_fwd")
+    with torch.cuda.device(dev):
+        _check(lib.tra_linear_attn_fwd(*(ctypes.byref(d) for d in descs), float(eps), _ptr(workspace),
+                                       workspace.numel(), _stream_handle(st)), "tra_linear_attn_fwd")
     return out
 
 
 def linear_attn_workspace_bytes(B: int, H: int, n: int, D: int) -> int:
     return int(load_library().tra_linear_attn_workspace_bytes(B, H, n, D))
+
+
+def _need_gate_x(x, w):
+    if not isinstance(x, torch.Tensor) or x.dim() != 3:
+        _fail("expected x as a [B, N, C] tensor")
+    _need_tensor("x", x, None, dtype=torch.bfloat16)
+    dev = x.device
+    B, N, C = x.shape
+    _need_tensor("w", w, dev, dtype=torch.bfloat16, shape=(C,), contiguous=True)
+    if w.numel() and w.data_ptr() % 16:
+        _fail("w data must be 16-byte aligned")
+    return dev, B, N, C
 
 
 def salad_gate(x: torch.Tensor, w: torch.Tensor, bias: float = 0.0, gate: torch.Tensor | None = None,
@@ -383,18 +511,19 @@ def salad_gate(x: torch.Tensor, w: torch.Tensor, bias: float = 0.0, gate: torch.
     `gate` ([B] float32, a new tensor by default).
     """
     lib = load_library()
-    if x.dim() != 3:
-        raise ValueError("expected x as [B, N, C]")
-    B, N, C = x.shape
+    dev, B, N, C = _need_gate_x(x, w)
+    st = _call_stream(stream, dev)
     need = int(lib.tra_salad_gate_workspace_bytes(B, N))
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+        workspace = _new(max(need, 256), torch.uint8, dev, st)
+    _need_workspace("workspace", workspace, dev, need)
     if gate is None:
-        gate = torch.empty(B, dtype=torch.float32, device=x.device)
+        gate = _new((B,), torch.float32, dev, st)
+    _need_tensor("gate", gate, dev, dtype=torch.float32, shape=(B,), contiguous=True)
     xd = _desc(x.unsqueeze(1))
-    _check(lib.tra_salad_gate(ctypes.byref(xd), ctypes.c_void_p(w.data_ptr()), float(bias),
-                              ctypes.c_void_p(gate.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
-                              workspace.numel(), _stream_handle(stream)), "tra_salad_gate")
+    with torch.cuda.device(dev):
+        _check(lib.tra_salad_gate(ctypes.byref(xd), _ptr(w), float(bias), _ptr(gate), _ptr(workspace),
+                                  workspace.numel(), _stream_handle(st)), "tra_salad_gate")
     return gate
 
 
@@ -406,14 +535,15 @@ def probe_mfma_peak(iterations: int = 200000, blocks: int | None = None, stream=
     """Measured bf16 MFMA peak (see tra_probe_mfma_peak): runs the register-only
     MFMA loop once per compute unit and returns (milliseconds, flops)."""
     lib = load_library()
+    dev = torch.device("cuda", torch.cuda.current_device())
     if blocks is None:
-        blocks = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
-    out = torch.empty(blocks, dtype=torch.float32, device="cuda")
+        blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    st = _call_stream(stream, dev)
+    out = _new((blocks,), torch.float32, dev, st)
     flops = ctypes.c_int64(0)
-    st = torch.cuda.current_stream() if stream is None else stream
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
-    _check(lib.tra_probe_mfma_peak(int(iterations), int(blocks), ctypes.c_void_p(out.data_ptr()), ctypes.byref(flops),
+    _check(lib.tra_probe_mfma_peak(int(iterations), int(blocks), _ptr(out), ctypes.byref(flops),
                                    _stream_handle(st)), "tra_probe_mfma_peak")
     e1.record(st)
     e1.synchronize()
@@ -430,12 +560,25 @@ def salad_combine(o_sparse: torch.Tensor, o_lin: torch.Tensor, weight: torch.Ten
     `out` defaults to a new tensor; it may be o_sparse itself.
     """
     lib = load_library()
+    _need_bhnd("o_sparse", o_sparse, None, dtype=torch.bfloat16)
+    dev = o_sparse.device
+    B, H, N, D = o_sparse.shape
+    C = H * D
+    _need_bhnd("o_lin", o_lin, dev, dtype=torch.bfloat16, shape=o_sparse.shape)
+    _need_tensor("weight", weight, dev, dtype=torch.bfloat16, shape=(C, C), contiguous=True)
+    _need_tensor("gate", gate, dev, dtype=torch.float32, shape=(B,), contiguous=True)
+    if bias is not None:
+        _need_tensor("bias", bias, dev, dtype=torch.float32, shape=(C,), contiguous=True)
+    for name, t in (("weight", weight), ("bias", bias)):
+        if t is not None and t.numel() and t.data_ptr() % 16:
+            _fail(f"{name} data must be 16-byte aligned")
+    st = _call_stream(stream, dev)
     if out is None:
-        out = torch.empty(o_sparse.shape, dtype=o_sparse.dtype, device=o_sparse.device)
+        out = _new(o_sparse.shape, o_sparse.dtype, dev, st)
+    _need_bhnd("out", out, dev, dtype=torch.bfloat16, shape=o_sparse.shape)
     descs = [_desc(t) for t in (o_sparse, o_lin, out)]
-    _check(lib.tra_salad_combine(ctypes.byref(descs[0]), ctypes.byref(descs[1]),
-                                 ctypes.c_void_p(weight.data_ptr()),
-                                 ctypes.c_void_p(None if bias is None else bias.data_ptr()),
-                                 ctypes.c_void_p(gate.data_ptr()), ctypes.byref(descs[2]),
-                                 _stream_handle(stream)), "tra_salad_combine")
+    with torch.cuda.device(dev):
+        _check(lib.tra_salad_combine(ctypes.byref(descs[0]), ctypes.byref(descs[1]), _ptr(weight), _ptr(bias),
+                                     _ptr(gate), ctypes.byref(descs[2]), _stream_handle(st)),
+               "tra_salad_combine")
     return out

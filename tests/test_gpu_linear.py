@@ -2,6 +2,8 @@
 per-row form.  bf16 inputs, fp32 accumulation, the d x d summary applied as
 a bf16 pair, O in bf16: max |dO| <= 2e-2 and relative RMS <= 1e-2.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -53,13 +55,21 @@ def test_linear_headline_shape(tra):
 def test_linear_errors(tra):
     q = torch.zeros((1, 1, 128, 64), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(16, dtype=torch.uint8, device="cuda")
-    with pytest.raises(tra.TraError) as e:
-        tra.linear_attn_fwd(q, q, q, workspace=ws)
-    assert e.value.status == -1  # workspace too small
-    with pytest.raises(tra.TraError) as e:
+    with pytest.raises(ValueError, match="holds 16 bytes"):
+        tra.linear_attn_fwd(q, q, q, workspace=ws)  # workspace too small
+    with pytest.raises(ValueError, match="dtype"):
         tra.linear_attn_fwd(q.float(), q.float(), q.float())
-    assert e.value.status == -2
     assert tra.linear_attn_workspace_bytes(1, 1, 128, 96) == 0
+    # the library refuses the same on its own (called directly)
+    lib = tra.load_library()
+    d = tra._desc(q)
+    r = ctypes.byref
+    assert lib.tra_linear_attn_fwd(r(d), r(d), r(d), r(d), 1e-6, ctypes.c_void_p(ws.data_ptr()), 16, None) == -1
+    f = tra._desc(q.float())
+    need = tra.linear_attn_workspace_bytes(1, 1, 128, 64)
+    big = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    assert lib.tra_linear_attn_fwd(r(f), r(f), r(f), r(f), 1e-6, ctypes.c_void_p(big.data_ptr()), need,
+                                   None) == -2
 
 
 def test_linear_strided_views(tra):
