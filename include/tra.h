@@ -163,11 +163,10 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
  * tra_sparse_attn_fwd -- O = softmax((Q K^T + M) * scale) V  (eq. 2).
  *
  * Q, K, V, O: [B, H, N, D] views, one dtype for all four (TRA_BF16: bf16
- * inputs, fp32 accumulation, O rounded to nearest-even bf16, and the scores
- * taken from the queries multiplied by scale log2(e) and rounded to bf16
- * once, which moves a score by at most 2^-8 scale sum_i |q_i k_i|; TRA_F32:
- * fp32 throughout).  N == mask n; D in {64, 128}.  O must not overlap Q, K
- * or V.
+ * inputs taken as given, fp32 accumulation of the scores, exponentials and
+ * sums, the probabilities rounded to bf16 for the P V product, O rounded to
+ * nearest-even bf16; TRA_F32: fp32 throughout).  N == mask n; D in
+ * {64, 128}.  O must not overlap Q, K or V.
  * LSE: NULL or device float[B * H * N] (contiguous [B, H, N]) receiving the
  * natural log of each row's softmax denominator, ln sum_t exp(scale * q.k_t)
  * over kept keys.  scale <= 0 selects 1/sqrt(D).  Rows whose every key is
@@ -187,9 +186,9 @@ tra_status tra_sparse_attn_fwd(const tra_tensor *Q, const tra_tensor *K, const t
 
 /*
  * tra_sparse_attn_bwd_workspace_bytes -- device workspace bytes that
- * tra_sparse_attn_bwd needs for B x H heads of N rows of width D: per row
- * two fp32 values and the row of scaled queries in bf16 (2 D bytes), about
- * (8 + 2 D) B H N bytes.  Returns 0 for negative sizes or D not 64/128.
+ * tra_sparse_attn_bwd needs for B x H heads of N rows of width D: two fp32
+ * values per row, each array 256-byte aligned (about 8 B H N bytes).
+ * Returns 0 for negative sizes or D not 64/128.
  */
 size_t tra_sparse_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D);
 
@@ -201,16 +200,15 @@ size_t tra_sparse_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int6
  * LSE), dO the gradient of O and delta = rowsum(dO o O):
  *   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - delta),
  *   dK = scale dS^T Q,  dQ = scale dS K.
- * P is recomputed the way the bf16 forward computes it, from the queries
- * multiplied by scale log2(e) and rounded to bf16, so that its rows sum to 1
- * against the saved LSE; dK uses those rounded queries too (ln 2 dS^T of
- * them), which moves each of its terms by at most 2^-8 relative.
+ * P is recomputed the way the bf16 forward computes it (the raw dot
+ * products q.k in fp32, shifted by -LSE / scale and scaled into the
+ * exponential), so that its rows sum to 1 against the saved LSE.
  * Q, K, V, O, dO, dQ, dK, dV: [B, H, N, D] bf16 views (same rules as the
  * forward; the gradients are accumulated in fp32 and rounded to bf16).
  * O and LSE must be the forward outputs for these Q, K, V, mask and scale.
  * workspace: device memory of at least tra_sparse_attn_bwd_workspace_bytes
- * bytes, 256-byte aligned, owned by the caller; overwritten (it holds delta,
- * -LSE log2(e) and the scaled queries while the call runs).
+ * bytes, 256-byte aligned, owned by the caller; overwritten (it holds delta
+ * and -LSE / scale per row while the call runs).
  * The outputs must not overlap the inputs, the workspace or each other.
  * Asynchronous; allocates nothing; the same mask must not be used by a
  * concurrent call.  Results are deterministic (no atomics).  B == 0 or

@@ -101,25 +101,15 @@ __device__ inline void retire_group(uint32_t *queue)
     }
 }
 
-// Persistent launch: as many workgroups as can be resident, capped by the
-// number of work items.
-template <class Kern>
-hipError_t launch_persistent(Kern kern, int threads, long long items, const AttnArgs &a, hipStream_t st)
+// Persistent launch: as many workgroups as can be resident (cached per device
+// and kernel, see resident_workgroups), capped by the number of work items.
+template <class Kern, class Args>
+hipError_t launch_persistent(Kern kern, int threads, long long items, const Args &a, hipStream_t st)
 {
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
+    long long grid = 0;
+    const hipError_t err = resident_workgroups((const void *)kern, threads, &grid);
     if (err != hipSuccess)
         return err;
-    int cus = 0, per_cu = 0;
-    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (err != hipSuccess)
-        return err;
-    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0);
-    if (err != hipSuccess)
-        return err;
-    if (per_cu < 1)
-        per_cu = 1;
-    long long grid = (long long)cus * per_cu;
     if (grid > items)
         grid = items;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), 0, st, a);

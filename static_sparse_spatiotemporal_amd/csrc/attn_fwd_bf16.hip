@@ -4,14 +4,11 @@
 // Computes O = softmax((Q K^T + M) * scale) V (Radial Attention section 2,
 // eq. 2) over the kept 128 x 128 blocks of the static mask, with the
 // streaming softmax: running row maximum m and denominator l, the
-// accumulator rescaled by 2^(m_old - m_new) when the maximum grows.  Scores
-// are taken in units of log2 so that exp is v_exp_f32 (base 2): each query
-// is multiplied by scale * log2(e) once, when its fragments are loaded, and
-// rounded back to bf16 (relative error <= 2^-8 per element, so a score
-// q.k * scale moves by at most 2^-8 * scale * sum_i |q_i k_i|, and the LSE
-// by at most the largest such move over the row).  The score MFMAs start
-// from -m, the row maximum in use, instead of from 0, so that their output
-// goes straight into v_exp_f32 with no per-score VALU work before it.
+// accumulator rescaled when the maximum grows.  The score MFMAs take the
+// queries as given (exact bf16) and start from -m, the row maximum in use
+// (in units of the raw dot product), instead of from 0, so that their output
+// is the score relative to the maximum; one multiply by scale * log2(e) per
+// score then feeds v_exp_f32 (base 2).
 //
 // Mapping.  One workgroup = 8 wave64s (two per SIMD) = one work item of the
 // mask's pair schedule: two 128-query blocks whose kept key blocks largely
@@ -130,7 +127,9 @@ void attn_fwd_bf16(AttnArgs a)
     const int lq = lane & 31, hh = lane >> 5;
     const int N = a.N;
     const float c2 = a.scale_log2;
-    constexpr float kTau = 8.f;
+    // rescale only when a row maximum grows by more than 2^8 in the
+    // probabilities, i.e. by 8 / c2 in raw dot-product units
+    const float tau = 8.f / c2;
 
     // LDS byte offsets of this lane's operand fragments (tile-invariant).
     int koff[G::NKS];
@@ -182,17 +181,16 @@ void attn_fwd_bf16(AttnArgs a)
         if (active) {
             const int qr = q0 + lq < N ? q0 + lq : N - 1;
 #pragma unroll
-            for (int ks = 0; ks < G::NKS; ++ks) {
-                const bf16x8 raw = *(const bf16x8 *)(Qp + (int64_t)qr * a.sq[2] + ks * 16 + hh * 8);
-                qf[ks] = __builtin_convertvector(__builtin_convertvector(raw, f32x8) * c2, bf16x8);
-            }
+            for (int ks = 0; ks < G::NKS; ++ks)
+                qf[ks] = *(const bf16x8 *)(Qp + (int64_t)qr * a.sq[2] + ks * 16 + hh * 8);
         }
         f32x16 o[G::NDB];
 #pragma unroll
         for (int db = 0; db < G::NDB; ++db)
             o[db] = f32x16{};
-        // m: row maximum (log2 units), l: row sum; muse: the maximum the
-        // scores are taken relative to (0 while m is -inf).
+        // m: row maximum of the raw dot products q.k, l: row sum of
+        // 2^((q.k - muse) c2); muse: the maximum the scores are taken
+        // relative to (0 while m is -inf).
         float m = kNegInf, l = 0.f, muse = 0.f;
 
         // Tile u is in buffer (u - u0) & 1; the loop takes two tiles per
@@ -229,7 +227,7 @@ void attn_fwd_bf16(AttnArgs a)
             const char LDS_AS *tK = (const char LDS_AS *)(buf == 0 ? sK0 : sK1);
             const char LDS_AS *tV = (const char LDS_AS *)(buf == 0 ? sV0 : sV1);
 
-            // ---- S^T = K Q^T - muse: 128 keys x 32 queries ----
+            // ---- S^T = K Q^T - muse: 128 keys x 32 queries (raw dot products) ----
             f32x16 s[4];
             const f32x16 s0 = f32x16{} - muse;
             bf16x8 kf[2][4];
@@ -271,9 +269,9 @@ void attn_fwd_bf16(AttnArgs a)
                 for (int i = 0; i < 16; ++i)
                     mx = fmaxf(mx, s[kb4][i]);
             const float mt = lane_pair_max(mx) + muse;
-            if (__builtin_amdgcn_ballot_w64(mt > m + kTau)) {
+            if (__builtin_amdgcn_ballot_w64(mt > m + tau)) {
                 const float mn = fmaxf(m, mt);
-                const float alpha = __builtin_amdgcn_exp2f(m - (mn == kNegInf ? 0.f : mn));
+                const float alpha = __builtin_amdgcn_exp2f((m - (mn == kNegInf ? 0.f : mn)) * c2);
 #pragma unroll
                 for (int db = 0; db < G::NDB; ++db)
                     o[db] *= alpha;
@@ -296,7 +294,7 @@ void attn_fwd_bf16(AttnArgs a)
                 f32x8 pv;
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
-                    pv[x] = __builtin_amdgcn_exp2f(s[t >> 1][8 * (t & 1) + x]);
+                    pv[x] = __builtin_amdgcn_exp2f(s[t >> 1][8 * (t & 1) + x] * c2);
                     ls[x & 1] += pv[x];
                 }
                 pf[t] = __builtin_convertvector(pv, bf16x8);
@@ -330,7 +328,7 @@ void attn_fwd_bf16(AttnArgs a)
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        // ---- epilogue: O = acc / l, LSE = ln 2 * (m + log2 l) ----
+        // ---- epilogue: O = acc / l, LSE = ln 2 * (m c2 + log2 l) ----
         if (STREAM && active) {
             // normalised partial output and log2-sum-exp of this key split
             const float lt = lane_pair_sum(l);
@@ -350,7 +348,7 @@ void attn_fwd_bf16(AttnArgs a)
                         *(f32x4 *)(prow + db * 32 + 8 * i4 + 4 * hh) = v;
                     }
                 if (hh == 0)
-                    a.part_lse[r] = lt > 0.f ? m + __log2f(lt) : kNegInf;
+                    a.part_lse[r] = lt > 0.f ? m * c2 + __log2f(lt) : kNegInf;
             }
         } else if (active) {
             const float lt = lane_pair_sum(l);
@@ -369,7 +367,7 @@ void attn_fwd_bf16(AttnArgs a)
                         *(bf16x4 *)(orow + db * 32 + 8 * i4 + 4 * hh) = __builtin_convertvector(v, bf16x4);
                     }
                 if (a.lse && hh == 0)
-                    a.lse[(int64_t)bh * N + q] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : kNegInf;
+                    a.lse[(int64_t)bh * N + q] = lt > 0.f ? (m * c2 + __log2f(lt)) * kLn2 : kNegInf;
             }
         }
     };

@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <numeric>
 #include <vector>
@@ -193,6 +194,45 @@ void fill_attn_args(tra::AttnArgs &a, const tra_tensor *Q, const tra_tensor *K, 
 
 }  // namespace
 
+namespace tra {
+
+hipError_t resident_workgroups(const void *kern, int threads, long long *out)
+{
+    struct Entry {
+        const void *kern;
+        int dev, threads;
+        long long grid;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> table;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return err;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (const Entry &e : table)
+            if (e.kern == kern && e.dev == dev && e.threads == threads) {
+                *out = e.grid;
+                return hipSuccess;
+            }
+    }
+    int cus = 0, per_cu = 0;
+    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess)
+        return err;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0);
+    if (err != hipSuccess)
+        return err;
+    const long long grid = (long long)cus * (per_cu < 1 ? 1 : per_cu);
+    std::lock_guard<std::mutex> lock(mu);
+    table.push_back({kern, dev, threads, grid});
+    *out = grid;
+    return hipSuccess;
+}
+
+}  // namespace tra
+
 // Frame-streaming K/V cache (see tra_kvcache_create).
 struct tra_kvcache {
     int64_t B, H, s, D;
@@ -200,6 +240,7 @@ struct tra_kvcache {
     int device;
     int64_t appended;  // frames appended since creation or reset
     int32_t nsplit_max;
+    int32_t cus;  // compute units of the device (queried at create)
     __bf16 *ring_k, *ring_v;  // [B, H, window * s, D]
     float *part_o, *part_lse;
 };
@@ -638,8 +679,7 @@ tra_status tra_sparse_attn_bwd(const tra_tensor *Q, const tra_tensor *K, const t
     a.dv = dV->data;
     a.lse = LSE;
     a.delta = (float *)((char *)workspace + ws.delta);
-    a.nlse2 = (float *)((char *)workspace + ws.nlse2);
-    a.qs = (char *)workspace + ws.qs;
+    a.nlse = (float *)((char *)workspace + ws.nlse);
     for (int i = 0; i < 3; ++i) {
         a.s_o[i] = O->stride[i];
         a.s_do[i] = dO->stride[i];
@@ -677,6 +717,7 @@ tra_status tra_kvcache_create(int64_t B, int64_t H, int64_t s, int64_t D, int32_
     const size_t rows = (size_t)(B * H * s);
     tra_status st_ = TRA_OK;
     TRA_HIP(hipGetDevice(&c->device));
+    TRA_HIP(hipDeviceGetAttribute(&c->cus, hipDeviceAttributeMultiprocessorCount, c->device));
     TRA_HIP(dev_alloc(&c->ring_k, ring));
     TRA_HIP(dev_alloc(&c->ring_v, ring));
     TRA_HIP(dev_alloc(&c->part_o, (size_t)c->nsplit_max * rows * D));
@@ -786,8 +827,7 @@ tra_status tra_kvcache_attn(tra_kvcache *c, const tra_tensor *Q, tra_tensor *O, 
     // partial outputs and merging than they gain in parallelism (measured at
     // 16 heads x 256 tokens x 16 frames: 41.7 us with 512 workgroups, 25.0 us
     // with 128, 28.1 us with 64)
-    int cus = 256;
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->device);
+    const int cus = c->cus > 0 ? c->cus : 256;
     const int64_t base = c->B * c->H * a.stream_pairs;
     int64_t want = ((int64_t)cus / 2 + base - 1) / base;
     want = std::max<int64_t>(1, std::min<int64_t>(want, a.nkv_tiles));

@@ -98,6 +98,13 @@ struct tra_mask {
 
 namespace tra {
 
+// Workgroups of `kern` (launched with `threads` threads and no dynamic LDS)
+// that the current device holds at once: compute units times resident
+// workgroups per unit (at least one per unit).  Queried from the runtime once
+// per (device, kernel) and kept for the life of the process, so that a launch
+// costs no device queries.
+hipError_t resident_workgroups(const void *kern, int threads, long long *out);
+
 // Mask builder (mask_build.hip).  All enqueue on `st`.
 hipError_t launch_classify(const MaskDesc &m, int nqb, int nkb, uint8_t *cls, int32_t *cnt,
                            hipStream_t st);
@@ -148,15 +155,13 @@ struct BwdArgs {
     const void *o, *dout;
     void *dq, *dk, *dv;
     const float *lse;
-    // workspace: delta = rowsum(dO o O), nlse2 = -LSE log2(e) (fp32 per row),
-    // qs = the queries times scale log2(e) rounded to bf16 ([B H N, D] rows)
-    float *delta, *nlse2;
-    void *qs;
+    // workspace: delta = rowsum(dO o O) and nlse = -LSE / scale (fp32 per row)
+    float *delta, *nlse;
     int64_t s_o[3], s_do[3], s_dq[3], s_dk[3], s_dv[3];
 };
 // Byte offsets of the backward workspace's parts (256-byte aligned) and its size.
 struct BwdWorkspace {
-    size_t delta, nlse2, qs, bytes;
+    size_t delta, nlse, bytes;
 };
 BwdWorkspace bwd_workspace(int64_t B, int64_t H, int64_t N, int64_t D);
 hipError_t launch_attn_bwd_bf16(const BwdArgs &a, hipStream_t st);

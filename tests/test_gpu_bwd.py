@@ -135,11 +135,16 @@ def test_bwd_sampled_parity(tra, name):
 
 
 def test_bwd_headline_rows_and_identities(tra):
-    """n = 131072: sampled dQ rows against the oracle, and at full size the
-    identities sum_t dV[t] = sum_q dO[q] and sum_t dK[t] = 0 per head."""
+    """n = 131072: sampled dQ rows and the dK/dV rows of two key blocks of one
+    head against the oracle element by element, and at full size the
+    identities sum_t dV[t] = sum_q dO[q] and sum_t dK[t] = 0 per head.  Key
+    blocks 0 and 8 (position 0 of frames 0 and 1) are kept by the fewest
+    query blocks (278 and 284 of 1024; the oracle needs the softmax of each
+    such query: about a minute on the host)."""
     w = workloads.WORKLOADS[workloads.HEADLINE]
     q_rows = _rows(w.n, w.B, w.H, blocks=2, seed=3, per_block=(0, 77, 127))
-    (q, k, v, do), (dq, dk, dv) = compare(tra, w, q_rows=q_rows, k_rows=np.zeros((0, 3), np.int64))
+    k_rows = np.array([(0, 5, kb * 128 + r) for kb in (0, 8) for r in (0, 1, 63, 64, 100, 127)], np.int64)
+    (q, k, v, do), (dq, dk, dv) = compare(tra, w, q_rows=q_rows, k_rows=k_rows)
     sv = dv.double().sum(dim=2)
     so = do.double().sum(dim=2)
     sk = dk.double().sum(dim=2)
@@ -187,19 +192,17 @@ def test_bwd_errors(tra):
     q, k, v = workloads.make_qkv(w, device="cuda")
     mask = tra.build_mask(w.f, w.s, w.kind)
     out, lse = tra.sparse_attn_fwd(q, k, v, mask)
-    with pytest.raises(tra.TraError) as e:
-        tra.sparse_attn_bwd(q, k, v, out, lse, out, mask)
-    assert e.value.status == -2  # fp32 backward is not provided
+    with pytest.raises(ValueError, match="dtype"):
+        tra.sparse_attn_bwd(q, k, v, out, lse, out, mask)  # fp32 backward is not provided
     # bf16: a workspace one byte short, or off 256-byte alignment, is refused
     qb, kb, vb = (x.to(torch.bfloat16) for x in (q, k, v))
     ob, lb = tra.sparse_attn_fwd(qb, kb, vb, mask)
     need = tra.sparse_attn_bwd_workspace_bytes(*qb.shape)
-    assert need == 2 * 256 * ((4 * w.n + 255) // 256) + 2 * w.n * w.D
+    assert need == 2 * 256 * ((4 * w.n + 255) // 256)
     ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
-    for bad in (ws[:need - 1], ws[16:16 + need]):
-        with pytest.raises(tra.TraError) as e:
+    for bad, why in ((ws[:need - 1], "holds"), (ws[16:16 + need], "aligned")):
+        with pytest.raises(ValueError, match=why):
             tra.sparse_attn_bwd(qb, kb, vb, ob, lb, ob, mask, workspace=bad)
-        assert e.value.status == -1
     g1 = tra.sparse_attn_bwd(qb, kb, vb, ob, lb, ob, mask, workspace=ws[:need])
     g2 = tra.sparse_attn_bwd(qb, kb, vb, ob, lb, ob, mask)
     torch.cuda.synchronize()

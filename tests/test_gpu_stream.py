@@ -3,8 +3,8 @@
 After appending frame i, attention for frame i's queries must equal the rows
 of frame i of the TRA_MASK_SWA_CAUSAL attention over frames 0 .. i (the ring
 keeps only the last `window` frames, which are exactly the frames those rows
-keep).  Same tolerances as the forward (bf16: 2e-2 on O, the per-row bound
-of tests/tolerance.py on LSE).
+keep).  Same tolerances as the forward (bf16: 2e-2 on O, the per-row LSE
+tolerance of tests/tolerance.py).
 """
 import numpy as np
 import pytest
@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads
-from tests.tolerance import lse_bound
+from tests.tolerance import lse_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -52,7 +52,7 @@ def check_stream(tra, B, H, s, D, window, nframes, seed, check_frames=None, rows
         got_o = out[rows[:, 0], rows[:, 1], rows[:, 2] - i * s].float().cpu().numpy()
         got_l = lse[rows[:, 0], rows[:, 1], rows[:, 2] - i * s].cpu().numpy()
         dl = np.abs(got_l - ref_l)
-        eo, el = float(np.abs(got_o - ref_o).max()), float((dl / lse_bound(q[:, :, :n], k[:, :, :n], rows)).max())
+        eo, el = float(np.abs(got_o - ref_o).max()), float((dl / lse_tol(spec, "bf16", rows[:, 2])).max())
         print(f"         max|dO|={eo:.3e} max|dLSE|={float(dl.max()):.3e} (max/bound {el:.3f})", flush=True)
         errs.append((i, eo, el))
     cache.free()
@@ -131,7 +131,6 @@ def test_stream_errors(tra):
     with pytest.raises(tra.TraError) as e:
         cache.attn(q)
     assert e.value.status == -1  # nothing appended yet
-    with pytest.raises(tra.TraError) as e:
-        cache.append(q[:, :, :64], q[:, :, :64])
-    assert e.value.status == -3
+    with pytest.raises(ValueError, match="shape"):
+        cache.append(q[:, :, :64], q[:, :, :64])  # refused by the binding
     cache.free()

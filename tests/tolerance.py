@@ -2,60 +2,44 @@
 
 Test helper (not collected).
 
-O (the benchmark spec bound): max-abs 1e-4 for fp32 inputs, 2e-2 for bf16 inputs
+O (the stated bounds): max-abs 1e-4 for fp32 inputs, 2e-2 for bf16 inputs
 with fp32 accumulation.
 
-LSE, fp32 inputs: max-abs 1e-4.
+LSE (the natural log of a row's softmax denominator, eq. 2 of the Radial
+Attention page): a bound per row that depends only on the input dtype and on
+the mask, never on how the kernels compute,
 
-LSE, bf16 inputs: a bound per row, derived from the arithmetic of the bf16
-kernels.  They multiply each query by scale * log2(e) once and round the
-product to bf16, a relative error of at most 2^-8 per element (the unit
-roundoff of an 8-bit significand).  A score
-scale * q.k therefore moves by at most 2^-8 * scale * sum_i |q_i k_i|, which
-Cauchy-Schwarz bounds by 2^-8 * scale * |q| * |k|.  The log-sum-exp moves by
-no more than the largest move of its terms, so the bound of a row is
-2^-8 * scale * |q| * max_t |k_t| (largest key norm of the head), plus 1e-4
-for the fp32 accumulation.  The Q = 0 probe (every score exactly 0) and the
-rounded-query test (the oracle given the kernel's rounded queries) hold
-tighter: 1e-4.
+    tol(row) = min(T, 0.5 ln(1 + 128 / K(row))),
+
+with K(row) the number of keys the row keeps and T = 1e-4 for fp32 inputs,
+1e-3 for bf16 inputs (fp32 accumulation of the scores, exponentials and row
+sums).  The second term is there so that the plain comparison sees a block
+error: one dropped (or added) 128-key block takes its share w of the row's
+softmax mass away (or adds it), which moves the LSE by -ln(1 - w) (ln(1 + w));
+with the attention spread over the kept keys w is about 128 / K, and half of
+the smaller move, 0.5 ln(1 + 128 / K), lies below either.  At the n = 131072
+radial workload (35,584 to 55,680 kept keys per row) it is 1.15e-3 to 1.8e-3,
+so T binds there; on the radius workload (at most 243 keys per row) it is
+about 0.2.  The Q = 0 probe pins the mask independently: all scores are 0, so
+every row's LSE must equal ln K(row) to 1e-4.
 """
 from __future__ import annotations
 
 import numpy as np
-import torch
+
+import oracle
 
 TOL_O = {"f32": 1e-4, "bf16": 2e-2}
-TOL_LSE_EXACT = 1e-4
-QUERY_ROUNDING = 2.0 ** -8 * (1 + 2.0 ** -7)  # bf16 rounding of q * c, c itself rounded to fp32
+TOL_LSE = {"f32": 1e-4, "bf16": 1e-3}
+TOL_LSE_EXACT = 1e-4  # Q = 0 probe: LSE = ln K exactly up to rounding
 
 
-def lse_bound(q: torch.Tensor, k: torch.Tensor, rows: np.ndarray | None = None,
-              scale: float | None = None) -> np.ndarray:
-    """Per-row LSE bound for the rows compared: `rows` as (b, h, query)
-    triples, or None for every row in (b, h, query) order."""
-    B, H, n, D = q.shape
-    count = B * H * n if rows is None else len(rows)
-    if q.dtype != torch.bfloat16:
-        return np.full(count, TOL_LSE_EXACT)
-    if scale is None:
-        scale = 1.0 / np.sqrt(D)
-    kmax = k.float().norm(dim=-1).amax(dim=-1).double().cpu().numpy()  # [B, H]
-    qn = q.float().norm(dim=-1).double().cpu().numpy()                  # [B, H, n]
-    if rows is None:
-        per = qn * kmax[:, :, None]
-        per = per.reshape(-1)
-    else:
-        b, h, r = rows[:, 0], rows[:, 1], rows[:, 2]
-        per = qn[b, h, r] * kmax[b, h]
-    return TOL_LSE_EXACT + QUERY_ROUNDING * scale * per
-
-
-def rounded_query(q: torch.Tensor, scale: float | None = None) -> torch.Tensor:
-    """The bf16 queries the bf16 kernels compute with, scaled by
-    scale * log2(e) (an oracle given these and scale ln 2 evaluates the same
-    scores)."""
-    D = q.shape[-1]
-    if scale is None:
-        scale = 1.0 / np.sqrt(D)
-    c = np.float32(scale * 1.4426950408889634)
-    return (q.float() * float(c)).to(torch.bfloat16)
+def lse_tol(spec: oracle.MaskSpec, dtype: str, queries, block_keep: np.ndarray | None = None) -> np.ndarray:
+    """Per-row LSE tolerance for the query indices `queries` (any shape; the
+    bound depends on the query index only, since the mask is shared by every
+    batch and head)."""
+    queries = np.asarray(queries, dtype=np.int64)
+    kept = oracle.row_counts(spec, queries.reshape(-1), block_keep=block_keep).astype(np.float64)
+    assert np.all(kept > 0), "every row of these masks keeps its own key"
+    tol = np.minimum(TOL_LSE[dtype], 0.5 * np.log1p(128.0 / kept))
+    return tol.reshape(queries.shape)
