@@ -123,6 +123,50 @@ def cpu_baseline(w, q, k, v, mask_info, target_s: float):
     }
 
 
+# The other workloads of the benchmark set, timed beside the headline: the
+# element-exact radial mask (fp32), the 3-D token radius, the frame sliding
+# window (d = 64) and the f = 20 radial block mask.
+OTHER_WORKLOADS = ["radial_f8_s64_fp32", "radius3d_t8_h16_w16", "swa_f64_s256_w16", "radial_f20_s1536_block"]
+
+
+def time_forward(tra, workloads, name: str, dev, stream, calls: int = 50, warmup: int = 10) -> dict:
+    """One workload's forward: per-call HIP-event time on the launch stream
+    (mean and median), wall time per call over back-to-back calls, and the
+    kept-block rate and share of the bf16 peak, both from the event mean."""
+    import torch
+    w = workloads.WORKLOADS[name]
+    mask = tra.build_mask(w.f, w.s, w.kind, **w.mask_kwargs())
+    info = mask.info
+    q, k, v = workloads.make_qkv(w, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        tra.sparse_attn_fwd(q, k, v, mask, out=out, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        tra.sparse_attn_fwd(q, k, v, mask, out=out, lse=lse, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ev_ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        tra.sparse_attn_fwd(q, k, v, mask, out=out, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / calls
+    flops = 4.0 * w.D * 128 * 128 * info["kept_blocks"] * w.B * w.H
+    ms = float(ev_ms.mean())
+    mask.free()
+    rec = {"shape": f"{w.B}x{w.H}x{w.n}x{w.D} {w.dtype}",
+           "ms_event_mean": round(ms, 4), "ms_event_median": round(float(np.median(ev_ms)), 4),
+           "ms_wall_per_call": round(wall_ms, 4),
+           "tflops_kept_blocks": round(flops / (ms * 1e-3) / 1e12, 2)}
+    if w.dtype == "bf16":
+        rec["pct_bf16_peak"] = round(100 * flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +178,8 @@ def main():
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the measured-MFMA-peak loop (for profiled runs)")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip timing the other workloads of the benchmark set")
     ap.add_argument("--cpu-seconds", type=float, default=30.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 2 GiB device copy (counter calibration)")
@@ -384,6 +430,9 @@ def main():
                       "block_eq4_tflops": round(eflops / (eq4_ms * 1e-3) / 1e12, 2),
                       "block_eq4_pct_bf16_peak": round(100 * eflops / (eq4_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2)})
         m2.free()
+
+    if not args.no_others and name == workloads.HEADLINE:
+        extra["other_workloads"] = {o: time_forward(tra, workloads, o, dev, stream) for o in OTHER_WORKLOADS}
 
     cpu = None
     if not args.no_cpu_baseline:
