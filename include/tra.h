@@ -327,6 +327,22 @@ tra_status tra_linear_attn_fwd(const tra_tensor *Q, const tra_tensor *K, const t
 size_t tra_salad_gate_workspace_bytes(int64_t B, int64_t N);
 tra_status tra_salad_gate(const tra_tensor *X, const void *w, float bias, float *gate, void *workspace,
                           size_t workspace_bytes, void *hip_stream);
+
+/*
+ * tra_salad_gate_noalloc -- tra_salad_gate for callers that cannot allocate
+ * device memory or bring a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments (minus the
+ * workspace), checks, kernels and results (bit for bit) as tra_salad_gate;
+ * the partial sums go to a fixed array in the library's device memory
+ * (256 KB, 65536 floats, one copy per device, held until the process ends).
+ * Calls no allocating routine.  Limit: B * min(1024, ceil(N / 64)) <= 65536
+ * (any N when B <= 64); larger requests return TRA_ERR_UNSUPPORTED before
+ * anything is enqueued.  Every call on a device shares that array, so calls
+ * that overlap in time on one device (two streams, two threads) race; calls
+ * ordered on one stream are safe.  Errors: as tra_salad_gate (no workspace
+ * errors), TRA_ERR_UNSUPPORTED past the limit, TRA_ERR_HIP.
+ */
+tra_status tra_salad_gate_noalloc(const tra_tensor *X, const void *w, float bias, float *gate, void *hip_stream);
 tra_status tra_salad_combine(const tra_tensor *O_sparse, const tra_tensor *O_lin, const void *W, const float *bias,
                              const float *gate, tra_tensor *out, void *hip_stream);
 

@@ -21,7 +21,7 @@ import os
 import numpy as np
 import torch
 
-__all__ = ["build_mask", "sparse_attn_fwd", "sparse_attn_bwd", "sparse_attn_bwd_workspace_bytes", "linear_attn_fwd", "salad_gate", "salad_combine",
+__all__ = ["build_mask", "sparse_attn_fwd", "sparse_attn_bwd", "sparse_attn_bwd_workspace_bytes", "linear_attn_fwd", "salad_gate", "salad_gate_noalloc", "salad_combine",
            "KVCache", "Mask", "TraError", "library_path", "load_library", "probe_mfma_peak",
            "KINDS", "GRANULARITIES"]
 
@@ -107,6 +107,8 @@ def load_library():
     lib.tra_salad_gate_workspace_bytes.restype = ctypes.c_size_t
     lib.tra_salad_gate.argtypes = [P(TensorDesc), vp, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
     lib.tra_salad_gate.restype = ctypes.c_int
+    lib.tra_salad_gate_noalloc.argtypes = [P(TensorDesc), vp, ctypes.c_float, vp, vp]
+    lib.tra_salad_gate_noalloc.restype = ctypes.c_int
     lib.tra_salad_combine.argtypes = [P(TensorDesc), P(TensorDesc), vp, vp, vp, P(TensorDesc), vp]
     lib.tra_salad_combine.restype = ctypes.c_int
     lib.tra_kvcache_create.argtypes = [i64, i64, i64, i64, ctypes.c_int32, ctypes.c_int32, P(vp)]
@@ -524,6 +526,25 @@ def salad_gate(x: torch.Tensor, w: torch.Tensor, bias: float = 0.0, gate: torch.
     with torch.cuda.device(dev):
         _check(lib.tra_salad_gate(ctypes.byref(xd), _ptr(w), float(bias), _ptr(gate), _ptr(workspace),
                                   workspace.numel(), _stream_handle(st)), "tra_salad_gate")
+    return gate
+
+
+def salad_gate_noalloc(x: torch.Tensor, w: torch.Tensor, bias: float = 0.0, gate: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """salad_gate without a workspace (see tra_salad_gate_noalloc): the library
+    keeps the partial sums in a fixed device array, so the call allocates
+    nothing when `gate` is given.  Calls that overlap in time on one device
+    race on that array."""
+    lib = load_library()
+    dev, B, N, C = _need_gate_x(x, w)
+    st = _call_stream(stream, dev)
+    if gate is None:
+        gate = _new((B,), torch.float32, dev, st)
+    _need_tensor("gate", gate, dev, dtype=torch.float32, shape=(B,), contiguous=True)
+    xd = _desc(x.unsqueeze(1))
+    with torch.cuda.device(dev):
+        _check(lib.tra_salad_gate_noalloc(ctypes.byref(xd), _ptr(w), float(bias), _ptr(gate), _stream_handle(st)),
+               "tra_salad_gate_noalloc")
     return gate
 
 

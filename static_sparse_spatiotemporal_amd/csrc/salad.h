@@ -17,6 +17,16 @@ size_t salad_gate_workspace_bytes(int64_t B, int64_t N);
 hipError_t launch_salad_gate(const void *x, const int64_t sx[2], const void *w, float bias, int64_t B, int64_t N,
                              int64_t C, float *gate, void *workspace, hipStream_t stream);
 
+// The gate on the library's own scratch array (no allocation, no
+// workspace): kGateScratchFloats partial sums, enough for B samples of N
+// tokens while B * min(1024, ceil(N / 64)) <= kGateScratchFloats (any N for
+// B <= 64).  All calls on one device share the array: calls that overlap in
+// time on a device race.
+constexpr int64_t kGateScratchFloats = 65536;  // 256 KB per device
+bool salad_gate_scratch_fits(int64_t B, int64_t N);
+hipError_t launch_salad_gate_scratch(const void *x, const int64_t sx[2], const void *w, float bias, int64_t B,
+                                     int64_t N, int64_t C, float *gate, hipStream_t stream);
+
 // out = O_s + gate[b] * (O_l W^T + bias) over the merged-head channels; the
 // three tensors are [B, H, N, D] views with element strides s_*[0..2] for
 // B, H, N (unit stride in D).

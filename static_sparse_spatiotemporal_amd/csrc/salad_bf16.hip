@@ -16,6 +16,8 @@
 //                       XOR-swizzled rows.  Each wave then stages its fp32
 //                       result in LDS and reads O_s and writes out in
 //                       256-byte row pieces.
+#include <mutex>
+
 #include "attn_common.h"
 #include "salad.h"
 
@@ -352,6 +354,53 @@ hipError_t launch_salad_gate(const void *x, const int64_t sx[2], const void *w, 
                        (size_t)C * sizeof(__bf16), stream, a);
     hipLaunchKernelGGL(k_salad_gate_final, dim3((unsigned)B), dim3(64), 0, stream, a);
     return hipGetLastError();
+}
+
+// ------------------------------------------ gate without allocation ----
+
+// The gate's partial sums in a fixed device array, for callers that cannot
+// allocate or bring a workspace (code under graph capture, serving loops).
+// Each device holds its own copy until the process ends.  In host code the
+// name `scratch` is only a host-side stand-in: the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is ever passed to a kernel.
+static __device__ __align__(256) float scratch[kGateScratchFloats];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+}  // namespace
+
+bool salad_gate_scratch_fits(int64_t B, int64_t N)
+{
+    return B >= 0 && (int64_t)gate_parts(N) * B <= kGateScratchFloats;
+}
+
+hipError_t launch_salad_gate_scratch(const void *x, const int64_t sx[2], const void *w, float bias, int64_t B,
+                                     int64_t N, int64_t C, float *gate, hipStream_t stream)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    void *ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (g_scratch[dev] == nullptr) {
+            e = hipGetSymbolAddress(&g_scratch[dev], HIP_SYMBOL(scratch));
+            if (e != hipSuccess) {
+                g_scratch[dev] = nullptr;
+                return e;
+            }
+        }
+        ptr = g_scratch[dev];
+    }
+    // every (sample, part) slot is written by the part kernel before the
+    // final kernel reads it, so the array needs no clearing between calls
+    return launch_salad_gate(x, sx, w, bias, B, N, C, gate, ptr, stream);
 }
 
 hipError_t launch_salad_combine(const void *os, const int64_t s_os[3], const void *ol, const int64_t s_ol[3],

@@ -926,8 +926,8 @@ size_t tra_salad_gate_workspace_bytes(int64_t B, int64_t N)
     return tra::salad_gate_workspace_bytes(B, N);
 }
 
-tra_status tra_salad_gate(const tra_tensor *X, const void *w, float bias, float *gate, void *workspace,
-                          size_t workspace_bytes, void *hip_stream)
+// Checks shared by the two gate entry points (all but the workspace).
+static tra_status check_gate_args(const tra_tensor *X, const void *w, const float *gate)
 {
     if (X == nullptr)
         return TRA_ERR_INVALID;
@@ -951,12 +951,33 @@ tra_status tra_salad_gate(const tra_tensor *X, const void *w, float bias, float 
         return TRA_ERR_UNSUPPORTED;
     if (X->B >= 65536 || X->N >= ((int64_t)1 << 40))
         return TRA_ERR_UNSUPPORTED;
+    return TRA_OK;
+}
+
+tra_status tra_salad_gate(const tra_tensor *X, const void *w, float bias, float *gate, void *workspace,
+                          size_t workspace_bytes, void *hip_stream)
+{
+    const tra_status st = check_gate_args(X, w, gate);
+    if (st != TRA_OK || X->B == 0)
+        return st;
     if (workspace == nullptr || workspace_bytes < tra::salad_gate_workspace_bytes(X->B, X->N) ||
         ((uintptr_t)workspace) % 256 != 0)
         return TRA_ERR_INVALID;
     const int64_t sx[2] = {X->stride[0], X->stride[2]};
-    return hip_status(tra::launch_salad_gate(X->data, sx, w, bias, X->B, X->N, C, gate, workspace,
+    return hip_status(tra::launch_salad_gate(X->data, sx, w, bias, X->B, X->N, X->D, gate, workspace,
                                              (hipStream_t)hip_stream));
+}
+
+tra_status tra_salad_gate_noalloc(const tra_tensor *X, const void *w, float bias, float *gate, void *hip_stream)
+{
+    const tra_status st = check_gate_args(X, w, gate);
+    if (st != TRA_OK || X->B == 0)
+        return st;
+    if (!tra::salad_gate_scratch_fits(X->B, X->N))
+        return TRA_ERR_UNSUPPORTED;
+    const int64_t sx[2] = {X->stride[0], X->stride[2]};
+    return hip_status(tra::launch_salad_gate_scratch(X->data, sx, w, bias, X->B, X->N, X->D, gate,
+                                                     (hipStream_t)hip_stream));
 }
 
 tra_status tra_salad_combine(const tra_tensor *O_sparse, const tra_tensor *O_lin, const void *W, const float *bias,
