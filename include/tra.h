@@ -203,8 +203,11 @@ size_t tra_sparse_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int6
  * P is recomputed the way the bf16 forward computes it (the raw dot
  * products q.k in fp32, shifted by -LSE / scale and scaled into the
  * exponential), so that its rows sum to 1 against the saved LSE.
- * Q, K, V, O, dO, dQ, dK, dV: [B, H, N, D] bf16 views (same rules as the
- * forward; the gradients are accumulated in fp32 and rounded to bf16).
+ * Q, K, V, O, dO, dQ, dK, dV: [B, H, N, D] views of one dtype (same rules
+ * as the forward).  TRA_BF16: MFMA products of bf16 operands (P and dS
+ * rounded to bf16), fp32 accumulation, gradients rounded to bf16.  TRA_F32:
+ * fp32 arithmetic throughout (vector ALU; meant for the small fp32
+ * workloads).
  * O and LSE must be the forward outputs for these Q, K, V, mask and scale.
  * workspace: device memory of at least tra_sparse_attn_bwd_workspace_bytes
  * bytes, 256-byte aligned, owned by the caller; overwritten (it holds delta
@@ -214,8 +217,8 @@ size_t tra_sparse_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int6
  * concurrent call.  Results are deterministic (no atomics).  B == 0 or
  * H == 0 returns TRA_OK.
  * Errors: TRA_ERR_INVALID (null tensor/mask/data/LSE/workspace, workspace
- * too small or misaligned), TRA_ERR_SHAPE, TRA_ERR_UNSUPPORTED (a dtype other
- * than bf16, D not 64/128, bad stride or alignment), TRA_ERR_HIP.
+ * too small or misaligned), TRA_ERR_SHAPE, TRA_ERR_UNSUPPORTED (mixed
+ * dtypes, D not 64/128, bad stride or alignment), TRA_ERR_HIP.
  */
 tra_status tra_sparse_attn_bwd(const tra_tensor *Q, const tra_tensor *K, const tra_tensor *V,
                                const tra_tensor *O, const tra_tensor *dO, const float *LSE,

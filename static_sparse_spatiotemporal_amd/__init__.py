@@ -358,17 +358,18 @@ def sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
                     workspace: torch.Tensor | None = None, stream=None):
     """Gradients (dQ, dK, dV) of sparse_attn_fwd on the GPU (see tra_sparse_attn_bwd).
 
-    q, k, v, out, dout: [B, H, n, D] bf16 cuda tensors; lse: the forward's
-    [B, H, n] fp32 output.  `grads` = (dq, dk, dv) output tensors (default:
-    new contiguous ones); `workspace` a uint8 cuda tensor of at least
+    q, k, v, out, dout: [B, H, n, D] cuda tensors of one dtype (bf16 or
+    fp32); lse: the forward's [B, H, n] fp32 output.  `grads` = (dq, dk, dv)
+    output tensors of that dtype (default: new contiguous ones);
+    `workspace` a uint8 cuda tensor of at least
     sparse_attn_bwd_workspace_bytes bytes (default: new).
     """
     lib = load_library()
-    _need_bhnd("q", q, None, dtype=torch.bfloat16)
+    _need_bhnd("q", q, None, dtype=(torch.bfloat16, torch.float32))
     dev = q.device
     B, H, n, D = q.shape
     for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
-        _need_bhnd(name, t, dev, dtype=torch.bfloat16, shape=q.shape)
+        _need_bhnd(name, t, dev, dtype=q.dtype, shape=q.shape)
     _need_tensor("lse", lse, dev, dtype=torch.float32, shape=q.shape[:3], contiguous=True)
     st = _call_stream(stream, dev)
     if grads is None:
@@ -376,7 +377,7 @@ def sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     if len(grads) != 3:
         _fail("grads must be (dq, dk, dv)")
     for name, t in zip(("dq", "dk", "dv"), grads):
-        _need_bhnd(name, t, dev, dtype=torch.bfloat16, shape=q.shape)
+        _need_bhnd(name, t, dev, dtype=q.dtype, shape=q.shape)
     need = int(lib.tra_sparse_attn_bwd_workspace_bytes(B, H, n, D))
     if workspace is None:
         workspace = _new(max(need, 1), torch.uint8, dev, st)

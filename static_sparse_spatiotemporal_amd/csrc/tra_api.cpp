@@ -639,17 +639,20 @@ tra_status tra_sparse_attn_bwd(const tra_tensor *Q, const tra_tensor *K, const t
     }
     if (Q->N != mask->info.n)
         return TRA_ERR_SHAPE;
+    if (Q->dtype != TRA_BF16 && Q->dtype != TRA_F32)
+        return TRA_ERR_UNSUPPORTED;
     for (int i = 0; i < 8; ++i)
-        if (ts[i]->dtype != TRA_BF16)
+        if (ts[i]->dtype != Q->dtype)
             return TRA_ERR_UNSUPPORTED;
     if (Q->D != 64 && Q->D != 128)
         return TRA_ERR_UNSUPPORTED;
+    const int64_t vec = Q->dtype == TRA_BF16 ? 8 : 4;  // elements per 16 bytes
     for (int i = 0; i < 8; ++i) {
         const tra_tensor *t = ts[i];
         if (t->stride[3] != 1)
             return TRA_ERR_UNSUPPORTED;
         for (int j = 0; j < 3; ++j)
-            if (t->stride[j] < 0 || t->stride[j] % 8 != 0)
+            if (t->stride[j] < 0 || t->stride[j] % vec != 0)
                 return TRA_ERR_UNSUPPORTED;
         if (((uintptr_t)t->data) % 16 != 0)
             return TRA_ERR_UNSUPPORTED;
@@ -687,7 +690,8 @@ tra_status tra_sparse_attn_bwd(const tra_tensor *Q, const tra_tensor *K, const t
         a.s_dk[i] = dK->stride[i];
         a.s_dv[i] = dV->stride[i];
     }
-    return hip_status(tra::launch_attn_bwd_bf16(a, (hipStream_t)hip_stream));
+    return hip_status(Q->dtype == TRA_BF16 ? tra::launch_attn_bwd_bf16(a, (hipStream_t)hip_stream)
+                                           : tra::launch_attn_bwd_f32(a, (hipStream_t)hip_stream));
 }
 
 tra_status tra_kvcache_create(int64_t B, int64_t H, int64_t s, int64_t D, int32_t window, int32_t dtype,

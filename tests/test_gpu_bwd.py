@@ -1,11 +1,16 @@
 """GPU backward (dQ, dK, dV) vs the fp64 oracle through the C ABI.
 
-Tolerance: the gradients are accumulated in fp32 from bf16 inputs with the
+Tolerance, bf16 inputs: the gradients are accumulated in fp32 with the
 probabilities and dS rounded to bf16 for the MFMA products, and are returned
 in bf16, whose rounding alone is up to 2^-8 relative; every gradient element must
 lie within 2e-2 * max(1, max |reference|) of the oracle and the relative RMS
 error of each gradient must stay below 1e-2 (measured: 2.3e-3 to 2.5e-3).
+fp32 inputs: fp32 arithmetic throughout, so the bound is the forward's fp32
+bound on O, 1e-4 * max(1, max |reference|) per element, and relative RMS at
+most 1e-5 (sums of up to a few hundred fp32 products, each rounded at 2^-24).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -30,12 +35,6 @@ def spec_of(w):
                            r_t=w.r_t, r_s=w.r_s, window=w.window, sink_frames=w.sink_frames)
 
 
-def make_dout(w):
-    g = torch.Generator(device="cuda")
-    g.manual_seed(w.seed + 7)
-    return torch.randn((w.B, w.H, w.n, w.D), generator=g, device="cuda").to(torch.bfloat16)
-
-
 def run_bwd(tra, w, mask):
     q, k, v = workloads.make_qkv(w, device="cuda")
     do = make_dout(w)
@@ -45,8 +44,18 @@ def run_bwd(tra, w, mask):
     return (q, k, v, do), (dq, dk, dv)
 
 
-def tol(ref):
-    return 2e-2 * max(1.0, float(np.abs(ref).max()))
+TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-5)}  # (per element x max(1, max|ref|), relative RMS)
+
+
+def make_dout(w):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed + 7)
+    d = torch.randn((w.B, w.H, w.n, w.D), generator=g, device="cuda")
+    return d.to(torch.bfloat16) if w.dtype == "bf16" else d
+
+
+def tol(ref, dtype="bf16"):
+    return TOL[dtype][0] * max(1.0, float(np.abs(ref).max()))
 
 
 def compare(tra, w, q_rows=None, k_rows=None, tag=""):
@@ -69,11 +78,11 @@ def compare(tra, w, q_rows=None, k_rows=None, tag=""):
         rel = float(np.sqrt(((g - ref) ** 2).sum() / max((ref ** 2).sum(), 1e-30))) if ref.size else 0.0
         print(f"       {name}: max|err|={e:.3e} rel-rms={rel:.2e} max|ref|={np.abs(ref).max() if ref.size else 0:.3f}",
               flush=True)
-        errs.append((name, e, tol(ref) if ref.size else 1.0))
+        errs.append((name, e, tol(ref, w.dtype) if ref.size else 1.0))
         if ref.size and float(np.abs(ref).max()) > 1e-3:
-            # the bf16 rounding of the outputs and of P and dS gives about
+            # bf16: the rounding of the outputs and of P and dS gives about
             # 2.4e-3; a wrong term or sign would give O(1)
-            assert rel <= 1e-2, (name, rel)
+            assert rel <= TOL[w.dtype][1], (name, rel)
     for name, e, t in errs:
         assert e <= t, (name, e, t)
     return (q, k, v, do), (dq, dk, dv)
@@ -104,6 +113,30 @@ def test_bwd_full_parity(tra, case):
         # one key per row: P = 1 and dP = delta = dO . V, so dS vanishes up to
         # the fp32 rounding of two sums of the same D products
         assert float(dq.float().abs().max()) <= 1e-4 and float(dk.float().abs().max()) <= 1e-4
+
+
+F32_CASES = [
+    # (kind, f, s, granularity, extra, B, H, D)
+    ("radial", 10, 50, "element", {}, 1, 2, 64),
+    ("radial", 7, 100, "block_any", {}, 1, 2, 128),
+    ("swa", 9, 37, "element", dict(window=3), 2, 1, 128),
+    ("radius3d", 3, 100, "element", dict(grid_h=10, grid_w=10, r_t=1, r_s=2), 1, 2, 64),
+    ("radial", 12, 256, "block_eq4", dict(sink_frames=1), 1, 1, 64),
+    ("dense", 3, 100, "element", {}, 1, 1, 128),
+]
+
+
+def test_bwd_f32_workload(tra):
+    """The fp32 workload (radial eq. 4 element mask, f = 8 x s = 64, d = 64):
+    every gradient row against the oracle at the fp32 bound."""
+    compare(tra, workloads.WORKLOADS["radial_f8_s64_fp32"])
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: f"{c[0]}-f{c[1]}-s{c[2]}-{c[3]}-D{c[7]}")
+def test_bwd_f32_full_parity(tra, case):
+    kind, f, s, gran, extra, B, H, D = case
+    w = workloads.Workload(f"{kind}_f{f}_s{s}", kind, gran, f, s, B, H, D, "f32", seed=6160 + f + s + D, **extra)
+    compare(tra, w)
 
 
 def test_bwd_radius_workload(tra):
@@ -167,11 +200,12 @@ def test_bwd_deterministic(tra):
         assert torch.equal(a, b)
 
 
-def test_bwd_strided_views(tra):
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f32", 64)])
+def test_bwd_strided_views(tra, dt, D):
     """Q, K, V, O, dO as [B, H, n, D] views of [B, n, H, D] storage and the
     gradients written into such views give the contiguous run's gradients
     bit for bit (the kernels take strides, the arithmetic is the same)."""
-    w = workloads.Workload("radial_f6_s256", "radial", "block_any", 6, 256, 2, 3, 128, "bf16", seed=61)
+    w = workloads.Workload("radial_f6_s256", "radial", "block_any", 6, 256, 2, 3, D, dt, seed=61)
     mask = tra.build_mask(w.f, w.s, w.kind, **w.mask_kwargs())
     (q, k, v, do), (dq, dk, dv) = run_bwd(tra, w, mask)
     out, lse = tra.sparse_attn_fwd(q, k, v, mask)
@@ -193,7 +227,14 @@ def test_bwd_errors(tra):
     mask = tra.build_mask(w.f, w.s, w.kind)
     out, lse = tra.sparse_attn_fwd(q, k, v, mask)
     with pytest.raises(ValueError, match="dtype"):
-        tra.sparse_attn_bwd(q, k, v, out, lse, out, mask)  # fp32 backward is not provided
+        tra.sparse_attn_bwd(q, k, v, out, lse, out.to(torch.bfloat16), mask)  # mixed dtypes
+    lib = tra.load_library()
+    ds = [tra._desc(t) for t in (q, k, v, out, out.to(torch.bfloat16), out, out, out)]
+    ws0 = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    r = ctypes.byref
+    assert lib.tra_sparse_attn_bwd(*(r(d) for d in ds[:5]), ctypes.c_void_p(lse.data_ptr()), mask.handle,
+                                   *(r(d) for d in ds[5:]), ctypes.c_void_p(ws0.data_ptr()), ws0.numel(), 0.0,
+                                   None) == -2  # the library refuses mixed dtypes too
     # bf16: a workspace one byte short, or off 256-byte alignment, is refused
     qb, kb, vb = (x.to(torch.bfloat16) for x in (q, k, v))
     ob, lb = tra.sparse_attn_fwd(qb, kb, vb, mask)
