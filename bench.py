@@ -157,13 +157,28 @@ def time_forward(tra, workloads, name: str, dev, stream, calls: int = 50, warmup
     wall_ms = (time.perf_counter() - t0) * 1e3 / calls
     flops = 4.0 * w.D * 128 * 128 * info["kept_blocks"] * w.B * w.H
     ms = float(ev_ms.mean())
-    mask.free()
     rec = {"shape": f"{w.B}x{w.H}x{w.n}x{w.D} {w.dtype}",
            "ms_event_mean": round(ms, 4), "ms_event_median": round(float(np.median(ev_ms)), 4),
            "ms_wall_per_call": round(wall_ms, 4),
            "tflops_kept_blocks": round(flops / (ms * 1e-3) / 1e12, 2)}
     if w.dtype == "bf16":
         rec["pct_bf16_peak"] = round(100 * flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2)
+    # backward on the same mask and inputs (gradients from the saved LSE)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 7)
+    dout = torch.randn(q.shape, generator=g, device=dev).to(q.dtype)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(max(1, tra.sparse_attn_bwd_workspace_bytes(*q.shape)), dtype=torch.uint8, device=dev)
+    tra.sparse_attn_bwd(q, k, v, out, lse, dout, mask, grads=grads, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        tra.sparse_attn_bwd(q, k, v, out, lse, dout, mask, grads=grads, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rec["bwd_ms_event_mean"] = round(e0.elapsed_time(e1) / 5, 4)
+    mask.free()
     return rec
 
 

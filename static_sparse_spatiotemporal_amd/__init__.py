@@ -15,6 +15,7 @@ neighbourhood on a t-h-w grid, or a frame sliding-window causal mask.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -172,13 +173,14 @@ def _need_tensor(name: str, t, device: torch.device | None, dtype=None, shape=No
     if device is None:
         if not t.is_cuda:
             _fail(f"{name} must be on a HIP device (got {t.device})")
-    elif t.device != device:
+    elif (not t.is_cuda or t.get_device() != device.index) if device.type == "cuda" else t.device != device:
         _fail(f"{name} is on {t.device}, the call runs on {device}")
     if dtype is not None:
-        ok = dtype if isinstance(dtype, tuple) else (dtype,)
-        if t.dtype not in ok:
-            _fail(f"{name} must have dtype {' or '.join(str(d) for d in ok)}, got {t.dtype}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+        td = t.dtype
+        if td is not dtype and (not isinstance(dtype, tuple) or td not in dtype):
+            ok = dtype if isinstance(dtype, tuple) else (dtype,)
+            _fail(f"{name} must have dtype {' or '.join(str(d) for d in ok)}, got {td}")
+    if shape is not None and t.shape != shape:
         _fail(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if contiguous and not t.is_contiguous():
         _fail(f"{name} must be contiguous")
@@ -194,11 +196,11 @@ def _need_bhnd(name: str, t, device: torch.device | None, dtype=None, shape=None
     if t.numel() == 0:
         return t
     vec = 16 // t.element_size()
-    st = t.stride()
-    if st[3] != 1 and t.shape[3] > 1:
+    s0, s1, s2, s3 = t.stride()
+    if s3 != 1 and t.shape[3] > 1:
         _fail(f"{name} must have unit stride in its last dimension")
-    if any(x < 0 or x % vec for x in st[:3]):
-        _fail(f"{name}: strides {tuple(st[:3])} must be multiples of {vec} elements (16 bytes)")
+    if s0 < 0 or s1 < 0 or s2 < 0 or s0 % vec or s1 % vec or s2 % vec:
+        _fail(f"{name}: strides {(s0, s1, s2)} must be multiples of {vec} elements (16 bytes)")
     if t.data_ptr() % 16:
         _fail(f"{name} data must be 16-byte aligned")
     return t
@@ -294,22 +296,39 @@ def build_mask(f: int, s: int, kind: str, granularity: str = "element", grid_h: 
     return Mask(h)
 
 
+_DT = {torch.bfloat16: _BF16, torch.float32: _F32}
+_STRIDES = ctypes.c_int64 * 4
+
+
+_DESC_CACHE: dict = {}
+
+
 def _desc(t: torch.Tensor) -> TensorDesc:
+    """The C view of a [B, H, N, D] tensor.  Views are memoised on everything
+    they hold (pointer, dtype, shape, strides), so a repeated call with the
+    same tensors skips building the ctypes structure; the library only reads
+    it during the call."""
+    key = (t.data_ptr(), t.dtype, t.shape, t.stride())
+    d = _DESC_CACHE.get(key)
+    if d is not None:
+        return d
     if t.dim() != 4:
         raise ValueError("expected a [B, H, N, D] tensor")
-    if t.dtype == torch.bfloat16:
-        dt = _BF16
-    elif t.dtype == torch.float32:
-        dt = _F32
-    else:
+    dt = _DT.get(t.dtype)
+    if dt is None:
         raise ValueError(f"unsupported dtype {t.dtype}")
-    d = TensorDesc()
-    d.data = t.data_ptr()
-    d.dtype = dt
-    d.B, d.H, d.N, d.D = t.shape
-    for i, st in enumerate(t.stride()):
-        d.stride[i] = st
+    B, H, N, D = t.shape
+    d = TensorDesc(t.data_ptr(), dt, 0, B, H, N, D, _STRIDES(*t.stride()))
+    if len(_DESC_CACHE) >= 512:
+        _DESC_CACHE.clear()
+    _DESC_CACHE[key] = d
     return d
+
+
+def _on(dev: torch.device):
+    """Makes `dev` the current device for the library call (only switches when
+    it is not current already)."""
+    return contextlib.nullcontext() if torch.cuda.current_device() == dev.index else torch.cuda.device(dev)
 
 
 def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
@@ -346,7 +365,7 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mas
     _need_bhnd("out", out, dev, dtype=q.dtype, shape=q.shape)
     lse = _lse_arg(lse, q, st)
     dq, dk, dv, do = _desc(q), _desc(k), _desc(v), _desc(out)
-    with torch.cuda.device(dev):
+    with _on(dev):
         _check(load_library().tra_sparse_attn_fwd(
             ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), mask.handle, ctypes.byref(do),
             _ptr(lse), float(scale) if scale else 0.0, _stream_handle(st)), "tra_sparse_attn_fwd")
@@ -384,7 +403,7 @@ def sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     _need_workspace("workspace", workspace, dev, need)
     descs = [_desc(t) for t in (q, k, v, out, dout)]
     gd = [_desc(t) for t in grads]
-    with torch.cuda.device(dev):
+    with _on(dev):
         _check(lib.tra_sparse_attn_bwd(
             *(ctypes.byref(d) for d in descs), _ptr(lse), mask.handle,
             *(ctypes.byref(d) for d in gd), _ptr(workspace), workspace.numel(),
@@ -421,7 +440,7 @@ class KVCache:
         _need_bhnd("v", v, self.device, dtype=torch.bfloat16, shape=self.shape)
         st = _call_stream(stream, self.device)
         dk, dv = _desc(k), _desc(v)
-        with torch.cuda.device(self.device):
+        with _on(self.device):
             _check(load_library().tra_kvcache_append(self.handle, ctypes.byref(dk), ctypes.byref(dv),
                                                      _stream_handle(st)), "tra_kvcache_append")
 
@@ -434,7 +453,7 @@ class KVCache:
         _need_bhnd("out", out, self.device, dtype=torch.bfloat16, shape=self.shape)
         lse = _lse_arg(lse, q, st)
         dq, do = _desc(q), _desc(out)
-        with torch.cuda.device(self.device):
+        with _on(self.device):
             _check(load_library().tra_kvcache_attn(
                 self.handle, ctypes.byref(dq), ctypes.byref(do), _ptr(lse),
                 float(scale) if scale else 0.0, _stream_handle(st)), "tra_kvcache_attn")
@@ -483,7 +502,7 @@ def linear_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
         out = _new(q.shape, q.dtype, dev, st)
     _need_bhnd("out", out, dev, dtype=torch.bfloat16, shape=q.shape)
     descs = [_desc(t) for t in (q, k, v, out)]
-    with torch.cuda.device(dev):
+    with _on(dev):
         _check(lib.tra_linear_attn_fwd(*(ctypes.byref(d) for d in descs), float(eps), _ptr(workspace),
                                        workspace.numel(), _stream_handle(st)), "tra_linear_attn_fwd")
     return out
@@ -524,7 +543,7 @@ def salad_gate(x: torch.Tensor, w: torch.Tensor, bias: float = 0.0, gate: torch.
         gate = _new((B,), torch.float32, dev, st)
     _need_tensor("gate", gate, dev, dtype=torch.float32, shape=(B,), contiguous=True)
     xd = _desc(x.unsqueeze(1))
-    with torch.cuda.device(dev):
+    with _on(dev):
         _check(lib.tra_salad_gate(ctypes.byref(xd), _ptr(w), float(bias), _ptr(gate), _ptr(workspace),
                                   workspace.numel(), _stream_handle(st)), "tra_salad_gate")
     return gate
@@ -543,7 +562,7 @@ def salad_gate_noalloc(x: torch.Tensor, w: torch.Tensor, bias: float = 0.0, gate
         gate = _new((B,), torch.float32, dev, st)
     _need_tensor("gate", gate, dev, dtype=torch.float32, shape=(B,), contiguous=True)
     xd = _desc(x.unsqueeze(1))
-    with torch.cuda.device(dev):
+    with _on(dev):
         _check(lib.tra_salad_gate_noalloc(ctypes.byref(xd), _ptr(w), float(bias), _ptr(gate), _stream_handle(st)),
                "tra_salad_gate_noalloc")
     return gate
@@ -599,7 +618,7 @@ def salad_combine(o_sparse: torch.Tensor, o_lin: torch.Tensor, weight: torch.Ten
         out = _new(o_sparse.shape, o_sparse.dtype, dev, st)
     _need_bhnd("out", out, dev, dtype=torch.bfloat16, shape=o_sparse.shape)
     descs = [_desc(t) for t in (o_sparse, o_lin, out)]
-    with torch.cuda.device(dev):
+    with _on(dev):
         _check(lib.tra_salad_combine(ctypes.byref(descs[0]), ctypes.byref(descs[1]), _ptr(weight), _ptr(bias),
                                      _ptr(gate), ctypes.byref(descs[2]), _stream_handle(st)),
                "tra_salad_combine")
