@@ -136,6 +136,10 @@ def load_library():
     lib.tra_last_hip_error.restype = ctypes.c_int32
     lib.tra_version.argtypes = []
     lib.tra_version.restype = ctypes.c_int32
+    lib.tra_debug_live_allocations.argtypes = []
+    lib.tra_debug_live_allocations.restype = ctypes.c_int64
+    lib.tra_debug_fail_allocations.argtypes = [ctypes.c_int64]
+    lib.tra_debug_fail_allocations.restype = ctypes.c_int64
     lib.tra_probe_mfma_peak.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p]
     lib.tra_probe_mfma_peak.restype = ctypes.c_int

@@ -1,6 +1,7 @@
 // C ABI of libtra.so: argument checking, mask compilation driver, attention
 // dispatch.  See include/tra.h for the contract of every entry point.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -10,6 +11,7 @@
 
 #include "probe.h"
 #include "salad.h"
+#include "tra_debug.h"
 #include "tra_internal.h"
 
 namespace {
@@ -33,114 +35,58 @@ tra_status hip_status(hipError_t e)
         }                                          \
     } while (0)
 
+// Every device buffer the library owns is allocated by dev_alloc and
+// released by dev_free, which count the live ones.  A test can make the
+// allocations fail from a given point on (tra_debug_fail_allocations) to run
+// the error paths.
+std::atomic<int64_t> g_live_allocs{0};
+std::atomic<int64_t> g_fail_after{-1};
+
 template <class T>
 hipError_t dev_alloc(T **p, size_t count)
 {
     *p = nullptr;
-    return hipMalloc((void **)p, std::max<size_t>(count, 1) * sizeof(T));
+    for (int64_t left = g_fail_after.load(); left >= 0;) {
+        if (left == 0)
+            return hipErrorOutOfMemory;
+        if (g_fail_after.compare_exchange_weak(left, left - 1))
+            break;
+    }
+    const hipError_t e = hipMalloc((void **)p, std::max<size_t>(count, 1) * sizeof(T));
+    if (e == hipSuccess)
+        ++g_live_allocs;
+    else
+        *p = nullptr;
+    return e;
 }
 
-// |A n B| / |A u B| of two ascending lists (1 for two empty lists).
-double jaccard(const int32_t *a, int na, const int32_t *b, int nb)
+void dev_free(void *p)
 {
-    int i = 0, j = 0, inter = 0;
-    while (i < na && j < nb) {
-        if (a[i] == b[j]) {
-            ++inter;
-            ++i;
-            ++j;
-        } else if (a[i] < b[j]) {
-            ++i;
-        } else {
-            ++j;
-        }
-    }
-    const int uni = na + nb - inter;
-    return uni ? (double)inter / uni : 1.0;
+    if (p != nullptr && hipFree(p) == hipSuccess)
+        --g_live_allocs;
 }
 
-// Host side of the pair schedule (see MaskDev): greedy pairing of query
-// blocks, in order, with the unpaired partner among r + 1 and r + s / 128
-// (same position in the next frame) that shares the most key blocks, if the
-// Jaccard overlap exceeds 1/2; then the merged key-block list of each pair.
-struct PairSchedule {
-    std::vector<int32_t> rows, ptr, col, em, order;
-};
-
-PairSchedule build_pairs(int nqb, int64_t s, const std::vector<int32_t> &row_ptr,
-                         const std::vector<int32_t> &col_idx, const std::vector<int32_t> &emask_idx)
-{
-    PairSchedule ps;
-    std::vector<int> offs = {1};
-    if (s % tra::kBlock == 0 && s / tra::kBlock > 1)
-        offs.push_back((int)(s / tra::kBlock));
-    std::vector<char> used(nqb, 0);
-    auto list = [&](int r) { return col_idx.data() + row_ptr[r]; };
-    auto len = [&](int r) { return row_ptr[r + 1] - row_ptr[r]; };
-    for (int r = 0; r < nqb; ++r) {
-        if (used[r])
-            continue;
-        int best = -1;
-        double bj = 0.5;
-        for (int off : offs) {
-            const int r2 = r + off;
-            if (r2 >= nqb || used[r2])
-                continue;
-            const double j = jaccard(list(r), len(r), list(r2), len(r2));
-            if (j > bj) {
-                bj = j;
-                best = r2;
-            }
-        }
-        used[r] = 1;
-        if (best >= 0)
-            used[best] = 1;
-        ps.rows.push_back(r);
-        ps.rows.push_back(best);
-    }
-    const int np = (int)ps.rows.size() / 2;
-    ps.ptr.assign(np + 1, 0);
-    for (int p = 0; p < np; ++p) {
-        const int a = ps.rows[2 * p], b = ps.rows[2 * p + 1];
-        int i = row_ptr[a], ie = row_ptr[a + 1];
-        int j = b >= 0 ? row_ptr[b] : 0, je = b >= 0 ? row_ptr[b + 1] : 0;
-        while (i < ie || j < je) {
-            const int ca = i < ie ? col_idx[i] : INT32_MAX;
-            const int cb = j < je ? col_idx[j] : INT32_MAX;
-            const int c = ca < cb ? ca : cb;
-            ps.col.push_back(c);
-            ps.em.push_back(ca == c ? emask_idx[i++] : tra::kAbsent);
-            ps.em.push_back(cb == c ? emask_idx[j++] : tra::kAbsent);
-        }
-        ps.ptr[p + 1] = (int32_t)ps.col.size();
-    }
-    ps.order.resize(np);
-    std::iota(ps.order.begin(), ps.order.end(), 0);
-    for (int c0 = 0; c0 < np; c0 += tra::kPairChunk)
-        std::stable_sort(ps.order.begin() + c0, ps.order.begin() + std::min(np, c0 + tra::kPairChunk),
-                         [&](int x, int y) { return ps.ptr[x + 1] - ps.ptr[x] > ps.ptr[y + 1] - ps.ptr[y]; });
-    return ps;
-}
+using tra::PairSchedule;
 
 void free_mask_buffers(tra_mask *m)
 {
-    (void)hipFree(m->bitmap);
-    (void)hipFree(m->row_ptr);
-    (void)hipFree(m->col_idx);
-    (void)hipFree(m->emask_idx);
-    (void)hipFree(m->emask);
-    (void)hipFree(m->order);
-    (void)hipFree(m->pair_rows);
-    (void)hipFree(m->pair_ptr);
-    (void)hipFree(m->u_col);
-    (void)hipFree(m->u_em);
-    (void)hipFree(m->pair_order);
-    (void)hipFree(m->queue);
-    (void)hipFree(m->t_pair_cols);
-    (void)hipFree(m->t_pair_ptr);
-    (void)hipFree(m->t_u_row);
-    (void)hipFree(m->t_u_em);
-    (void)hipFree(m->t_pair_order);
+    dev_free(m->bitmap);
+    dev_free(m->row_ptr);
+    dev_free(m->col_idx);
+    dev_free(m->emask_idx);
+    dev_free(m->emask);
+    dev_free(m->order);
+    dev_free(m->pair_rows);
+    dev_free(m->pair_ptr);
+    dev_free(m->u_col);
+    dev_free(m->u_em);
+    dev_free(m->pair_order);
+    dev_free(m->queue);
+    dev_free(m->t_pair_cols);
+    dev_free(m->t_pair_ptr);
+    dev_free(m->t_u_row);
+    dev_free(m->t_u_em);
+    dev_free(m->t_pair_order);
 }
 
 bool tensor_ok(const tra_tensor *t) { return t != nullptr && t->data != nullptr; }
@@ -268,6 +214,10 @@ const char *tra_status_string(tra_status s)
 
 int32_t tra_last_hip_error(void) { return g_last_hip_error; }
 
+int64_t tra_debug_live_allocations(void) { return g_live_allocs.load(); }
+
+int64_t tra_debug_fail_allocations(int64_t after) { return g_fail_after.exchange(after < 0 ? -1 : after); }
+
 int32_t tra_version(void) { return 100; /* 0.1.0 */ }
 
 tra_status tra_probe_mfma_peak(int64_t iterations, int32_t blocks, float *out, int64_t *flops, void *hip_stream)
@@ -384,10 +334,7 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
         h_part_ptr[r + 1] = (int32_t)npart;
     }
     // Within each chunk of kChunk consecutive query blocks, heaviest first.
-    std::iota(h_order.begin(), h_order.end(), 0);
-    for (int c0 = 0; c0 < nqb; c0 += tra::kChunk)
-        std::stable_sort(h_order.begin() + c0, h_order.begin() + std::min(nqb, c0 + tra::kChunk),
-                         [&](int x, int y) { return h_blocks[x] > h_blocks[y]; });
+    h_order = tra::chunk_order(std::vector<int64_t>(h_blocks.begin(), h_blocks.end()), tra::kChunk);
 
     TRA_HIP(dev_alloc(&m->row_ptr, nqb + 1));
     TRA_HIP(dev_alloc(&m->col_idx, (size_t)nnz));
@@ -414,7 +361,7 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
         TRA_HIP(hipMemcpy(h_col.data(), m->col_idx, nnz * sizeof(int32_t), hipMemcpyDeviceToHost));
         TRA_HIP(hipMemcpy(h_em.data(), m->emask_idx, nnz * sizeof(int32_t), hipMemcpyDeviceToHost));
     }
-    ps = build_pairs(nqb, s, h_row_ptr, h_col, h_em);
+    ps = tra::build_pairs(nqb, s, h_row_ptr, h_col, h_em);
     m->npairs = (int32_t)(ps.rows.size() / 2);
     TRA_HIP(dev_alloc(&m->pair_rows, ps.rows.size()));
     TRA_HIP(dev_alloc(&m->pair_ptr, ps.ptr.size()));
@@ -431,19 +378,9 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
 
     // The same schedule over key blocks, from the column lists of the mask.
     {
-        std::vector<int32_t> col_ptr(nkb + 1, 0), row_idx(nnz), em_t(nnz);
-        for (int64_t e = 0; e < nnz; ++e)
-            col_ptr[h_col[e] + 1]++;
-        for (int c = 0; c < nkb; ++c)
-            col_ptr[c + 1] += col_ptr[c];
-        std::vector<int32_t> fill(col_ptr.begin(), col_ptr.end() - 1);
-        for (int r = 0; r < nqb; ++r)  // rows in order: each column list ascends
-            for (int32_t e = h_row_ptr[r]; e < h_row_ptr[r + 1]; ++e) {
-                const int32_t at = fill[h_col[e]]++;
-                row_idx[at] = r;
-                em_t[at] = h_em[e];
-            }
-        tps = build_pairs(nkb, s, col_ptr, row_idx, em_t);
+        std::vector<int32_t> col_ptr, row_idx, em_t;
+        tra::transpose_csr(nqb, nkb, h_row_ptr, h_col, h_em, col_ptr, row_idx, em_t);
+        tps = tra::build_pairs(nkb, s, col_ptr, row_idx, em_t);
     }
     m->t_npairs = (int32_t)(tps.rows.size() / 2);
     m->t_nunion = (int64_t)tps.col.size();
@@ -485,27 +422,27 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
         in.bwd_work_items = m->t_npairs;
         in.bwd_tile_loads = m->t_nunion;
     }
-    (void)hipFree(cls);
-    (void)hipFree(cnt);
-    (void)hipFree(row_blocks);
-    (void)hipFree(row_partial);
-    (void)hipFree(row_pred);
-    (void)hipFree(row_eff);
-    (void)hipFree(part_ptr_d);
-    (void)hipFree(part_list);
+    dev_free(cls);
+    dev_free(cnt);
+    dev_free(row_blocks);
+    dev_free(row_partial);
+    dev_free(row_pred);
+    dev_free(row_eff);
+    dev_free(part_ptr_d);
+    dev_free(part_list);
     *out = m;
     return TRA_OK;
 
 fail:
     (void)hipStreamSynchronize(st);
-    (void)hipFree(cls);
-    (void)hipFree(cnt);
-    (void)hipFree(row_blocks);
-    (void)hipFree(row_partial);
-    (void)hipFree(row_pred);
-    (void)hipFree(row_eff);
-    (void)hipFree(part_ptr_d);
-    (void)hipFree(part_list);
+    dev_free(cls);
+    dev_free(cnt);
+    dev_free(row_blocks);
+    dev_free(row_partial);
+    dev_free(row_pred);
+    dev_free(row_eff);
+    dev_free(part_ptr_d);
+    dev_free(part_list);
     free_mask_buffers(m);
     delete m;
     return st_;
@@ -729,10 +666,10 @@ tra_status tra_kvcache_create(int64_t B, int64_t H, int64_t s, int64_t D, int32_
     *out = c;
     return TRA_OK;
 fail:
-    (void)hipFree(c->ring_k);
-    (void)hipFree(c->ring_v);
-    (void)hipFree(c->part_o);
-    (void)hipFree(c->part_lse);
+    dev_free(c->ring_k);
+    dev_free(c->ring_v);
+    dev_free(c->part_o);
+    dev_free(c->part_lse);
     delete c;
     return st_;
 }
@@ -865,10 +802,10 @@ void tra_kvcache_free(tra_kvcache *c)
 {
     if (c == nullptr)
         return;
-    (void)hipFree(c->ring_k);
-    (void)hipFree(c->ring_v);
-    (void)hipFree(c->part_o);
-    (void)hipFree(c->part_lse);
+    dev_free(c->ring_k);
+    dev_free(c->ring_v);
+    dev_free(c->part_o);
+    dev_free(c->part_lse);
     delete c;
 }
 

@@ -5,16 +5,13 @@
 #include <stdint.h>
 
 #include "tra.h"
+#include "tra_sched.h"
 
 namespace tra {
 
-constexpr int kBlock = 128;  // mask block edge (Radial Attention section 6)
-// Work distribution: query blocks are grouped in chunks of kChunk consecutive
-// blocks; chunk g of the (batch * head)-major chunk list belongs to the queue
-// of XCD g % kQueues.  The queue buffer holds kQueues counters and one
+// Per-XCD work queues (chunks of kChunk query blocks or kPairChunk pairs,
+// see tra_sched.h): the queue buffer holds kQueues counters and one
 // finished-workgroup counter.
-constexpr int kChunk = 64;      // query blocks per chunk (one per workgroup slot)
-constexpr int kPairChunk = 32;  // query-block pairs per chunk
 constexpr int kQueues = 8;
 constexpr int kQueueWords = 16;
 
@@ -29,10 +26,6 @@ struct MaskDesc {
 
 // Block class written by the classifier.
 enum : uint8_t { kEmpty = 0, kFull = 1, kPartial = 2 };
-
-// Emask index of a union-schedule entry for a query block that does not keep
-// the entry's key block.
-constexpr int32_t kAbsent = -2;
 
 // Device view of a compiled mask, passed to the attention kernels by value.
 //

@@ -1,13 +1,14 @@
 """C ABI checks that need no GPU: the library loads, exports every declared
 entry point, and rejects bad arguments on the host before any HIP call."""
 import ctypes
+import glob
 import os
 import re
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "tra.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 @pytest.fixture(scope="module")
@@ -17,16 +18,31 @@ def lib():
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tra_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for header in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+        names.update(re.findall(r"\b(tra_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(lib):
+    assert [os.path.basename(h) for h in HEADERS] == ["tra.h", "tra_debug.h"]
     names = _declared_functions()
     assert "tra_build_mask" in names and "tra_sparse_attn_fwd" in names
+    assert "tra_debug_fail_allocations" in names
     for name in names:
         assert hasattr(lib, name), name
+
+
+def test_allocation_hooks_on_host(lib):
+    """The failure-injection setting round-trips (negative = off) and
+    setting it allocates and releases nothing."""
+    live = lib.tra_debug_live_allocations()
+    assert live >= 0
+    assert lib.tra_debug_fail_allocations(3) == -1
+    assert lib.tra_debug_fail_allocations(-7) == 3
+    assert lib.tra_debug_fail_allocations(-1) == -1
+    assert lib.tra_debug_live_allocations() == live
 
 
 def test_status_strings_and_version(lib):
