@@ -200,9 +200,8 @@ size_t tra_sparse_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int6
  * LSE), dO the gradient of O and delta = rowsum(dO o O):
  *   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - delta),
  *   dK = scale dS^T Q,  dQ = scale dS K.
- * P is recomputed the way the bf16 forward computes it (the raw dot
- * products q.k in fp32, shifted by -LSE / scale and scaled into the
- * exponential), so that its rows sum to 1 against the saved LSE.
+ * P is recomputed from the raw dot products q.k in fp32 as
+ * exp(scale q.k - LSE), so that its rows sum to 1 against the saved LSE.
  * Q, K, V, O, dO, dQ, dK, dV: [B, H, N, D] views of one dtype (same rules
  * as the forward).  TRA_BF16: MFMA products of bf16 operands (P and dS
  * rounded to bf16), fp32 accumulation, gradients rounded to bf16.  TRA_F32:
@@ -211,7 +210,7 @@ size_t tra_sparse_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int6
  * O and LSE must be the forward outputs for these Q, K, V, mask and scale.
  * workspace: device memory of at least tra_sparse_attn_bwd_workspace_bytes
  * bytes, 256-byte aligned, owned by the caller; overwritten (it holds delta
- * and -LSE / scale per row while the call runs).
+ * and -LSE log2(e) per row while the call runs).
  * The outputs must not overlap the inputs, the workspace or each other.
  * Asynchronous; allocates nothing; the same mask must not be used by a
  * concurrent call.  Results are deterministic (no atomics).  B == 0 or

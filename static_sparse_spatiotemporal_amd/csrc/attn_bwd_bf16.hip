@@ -5,12 +5,12 @@
 // delta = rowsum(dO o O) = rowsum(P o dP):
 //   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - delta),
 //   dK = scale dS^T Q,   dQ = scale dS K.
-// P is recomputed as the forward computes it: raw dot products q.k of the
-// bf16 inputs (fp32 accumulation), shifted by -LSE / scale and multiplied by
-// scale * log2(e) before v_exp_f32, so that its rows sum to 1 against the
-// forward's LSE.
+// P is recomputed from the raw dot products q.k of the bf16 inputs (fp32
+// accumulation) as 2^(q.k scale log2(e) - LSE log2(e)), one fused
+// multiply-add per score before v_exp_f32, so that its rows sum to 1
+// against the forward's LSE.
 // Three kernels, no atomics (results are deterministic):
-//   k_bwd_prep   per row: delta and -LSE / scale (workspace);
+//   k_bwd_prep   per row: delta and -LSE log2(e) (workspace);
 //   k_bwd_dkdv   one workgroup per pair of key blocks (the mask's schedule
 //                over key blocks), 8 waves x 32 keys; streams the Q and dO
 //                tiles of every query block that keeps one of its key blocks
@@ -18,10 +18,9 @@
 //   k_bwd_dq     one workgroup per pair of query blocks (the forward's
 //                schedule), 8 waves x 32 queries; streams K and V tiles and
 //                accumulates dQ.
-// Both main kernels recompute S and dP with v_mfma_f32_32x32x16_bf16, the S
-// products starting from -LSE / scale instead of 0 (their output, times
-// scale * log2(e), goes straight into v_exp_f32), and keep the operand that
-// stays fixed for the workgroup (K and V, or Q and dO) in registers; the
+// Both main kernels recompute S and dP with v_mfma_f32_32x32x16_bf16 and
+// keep the operand that stays fixed for the workgroup (K and V, or Q and dO)
+// in registers; the
 // streamed tiles are copied HBM -> LDS with
 // global_load_lds_dwordx4 into double buffers (one LDS array each, named
 // statically in every step), XOR-swizzled so that both the row reads
@@ -172,7 +171,7 @@ __device__ inline void store_rows_t(__bf16 *X, int64_t stride, int row, int N, c
 // ---------------------------------------------------------------- prep
 
 // Per row r = (b, h, q), 8 lanes per row: delta[r] = sum_d dO[r, d] O[r, d]
-// and nlse[r] = -LSE[r] / scale (-inf for an empty row, whose probabilities
+// and nlse[r] = -LSE[r] log2(e) (-inf for an empty row, whose probabilities
 // are then 0).
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a)
@@ -202,7 +201,7 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a)
     if (r < rows && part == 0) {
         a.delta[r] = acc;
         const float l = a.lse[r];
-        a.nlse[r] = l == kNegInf ? kNegInf : -l / (a.f.scale_log2 / kLog2e);
+        a.nlse[r] = l == kNegInf ? kNegInf : -l * kLog2e;
     }
 }
 
@@ -211,8 +210,8 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a)
 // Workgroup = pair of key blocks; waves 0-3 own the first, 4-7 the second,
 // 32 keys each.  Per query tile and 32-query chunk c (lane = key, 16 queries
 // 32 c + 8 (i / 4) + 4 (lane / 32) + i % 4 per lane):
-//   S = Q K^T - LSE / scale and dP = dO V^T with K, V as register B
-//   operands; P = 2^(S scale log2 e), dS = P (dP - delta);
+//   S = Q K^T and dP = dO V^T with K, V as register B operands;
+//   P = 2^(S scale log2 e - LSE log2 e), dS = P (dP - delta);
 //   dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read transposed
 //   (dK = scale dK^T, transposed back, at the store).
 template <int D>
@@ -337,24 +336,24 @@ void k_bwd_dkdv(BwdArgs a)
                 // copies had been issued, and waiting for a reload then
                 // waited for those copies
                 const int lqc = ln & 31, hhc = ln >> 5;
-                // ---- S = Q K^T - LSE / scale, dP = dO V^T (32 queries x 32 keys) ----
-                // element i of this lane is query 32 c + 8 (i / 4) + 4 hh + i % 4
-                f32x16 s0;
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const f32x4 nl = *(const f32x4 LDS_AS *)(tL + c * 32 + 8 * r4 + 4 * hhc);
-#pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        s0[4 * r4 + x] = nl[x];
-                }
-                f32x16 s, dp = f32x16{};
+                // ---- S = Q K^T, dP = dO V^T (32 queries x 32 keys) ----
+                // element i of this lane is query 32 c + 8 (i / 4) + 4 hh + i % 4;
+                // operand fragments are read one k-step ahead
+                f32x16 s = f32x16{}, dp = f32x16{};
+                bf16x8 qa[2], ga[2];
+                qa[0] = *(const bf16x8 LDS_AS *)(tQ + cr + off.row(0));
+                ga[0] = *(const bf16x8 LDS_AS *)(tO + cr + off.row(0));
 #pragma unroll
                 for (int ks = 0; ks < G::NKS; ++ks) {
-                    const bf16x8 qa = *(const bf16x8 LDS_AS *)(tQ + cr + off.row(ks));
-                    const bf16x8 ga = *(const bf16x8 LDS_AS *)(tO + cr + off.row(ks));
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], ks == 0 ? s0 : s, 0, 0, 0);
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (ks + 1 < G::NKS) {
+                        qa[(ks + 1) & 1] = *(const bf16x8 LDS_AS *)(tQ + cr + off.row(ks + 1));
+                        ga[(ks + 1) & 1] = *(const bf16x8 LDS_AS *)(tO + cr + off.row(ks + 1));
+                    }
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks & 1], kf[ks], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks & 1], vf[ks], dp, 0, 0, 0);
                 }
+                __builtin_amdgcn_sched_barrier(0);
                 if (em >= 0) {
                     // base taken opaque in scalar registers here: hoisted, it
                     // was held in (spilled) vector registers across the loop.
@@ -382,11 +381,12 @@ void k_bwd_dkdv(BwdArgs a)
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
                     const f32x4 dl = *(const f32x4 LDS_AS *)(tD + c * 32 + 8 * r4 + 4 * hhc);
+                    const f32x4 nl = *(const f32x4 LDS_AS *)(tL + c * 32 + 8 * r4 + 4 * hhc);
                     f32x4 pv, dsv;
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
                         const int i = 4 * r4 + x;
-                        const float p = __builtin_amdgcn_exp2f(s[i] * c2);
+                        const float p = __builtin_amdgcn_exp2f(fmaf(s[i], c2, nl[x]));
                         pv[x] = p;
                         dsv[x] = p * (dp[i] - dl[x]);
                     }
@@ -428,8 +428,8 @@ void k_bwd_dkdv(BwdArgs a)
 
 // Workgroup = pair of query blocks (the forward's schedule); 32 queries per
 // wave.  Per key tile and 64-key half (lane = query, 32 keys per lane):
-//   S^T = K Q^T - LSE / scale and dP^T = V dO^T with Q, dO as register B
-//   operands; P = 2^(S scale log2 e), dS = P (dP - delta);
+//   S^T = K Q^T and dP^T = V dO^T with Q, dO as register B operands;
+//   P = 2^(S scale log2 e - LSE log2 e), dS = P (dP - delta);
 //   dQ^T += K^T dS^T with K^T read transposed.
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -533,15 +533,13 @@ void k_bwd_dq(BwdArgs a)
 
 #pragma unroll 1
             for (int hf = 0; hf < 2; ++hf) {
-                // ---- S^T = K Q^T - LSE / scale, dP^T = V dO^T: 64 keys x 32 queries ----
-                // rebuilt here (held across the loop it costs 16 registers)
-                float nlr = nl;
-                asm volatile("" : "+v"(nlr));
-                const f32x16 s0 = f32x16{} + nlr;
+                // ---- S^T = K Q^T, dP^T = V dO^T: 64 keys x 32 queries ----
                 f32x16 s[2], dp[2];
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb) {
+                    s[kb] = f32x16{};
                     dp[kb] = f32x16{};
+                }
 #pragma unroll
                 for (int ks = 0; ks < G::NKS; ++ks)
 #pragma unroll
@@ -549,7 +547,7 @@ void k_bwd_dq(BwdArgs a)
                         const int ro = (2 * hf + kb) * 32 * G::ROWB + off.row(ks);
                         const bf16x8 ka = *(const bf16x8 LDS_AS *)(tK + ro);
                         const bf16x8 va = *(const bf16x8 LDS_AS *)(tV + ro);
-                        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? s0 : s[kb], 0, 0, 0);
+                        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[kb], 0, 0, 0);
                         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], dp[kb], 0, 0, 0);
                     }
                 // element i of s[kb] is key 32 (2 hf + kb) + 8 (i / 4) + 4 hh + i % 4
@@ -570,7 +568,7 @@ void k_bwd_dq(BwdArgs a)
 #pragma unroll
                     for (int x = 0; x < 8; ++x) {
                         const int i = 8 * (t & 1) + x;
-                        const float p = __builtin_amdgcn_exp2f(s[t >> 1][i] * c2);
+                        const float p = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][i], c2, nl));
                         dsv[x] = p * (dp[t >> 1][i] - dl);
                     }
                     sb[t] = __builtin_convertvector(dsv, bf16x8);

@@ -148,8 +148,7 @@ struct BwdArgs {
     const void *o, *dout;
     void *dq, *dk, *dv;
     const float *lse;
-    // workspace: delta = rowsum(dO o O) and nlse = -LSE / scale (bf16
-    // kernels) or -LSE log2(e) (fp32 kernels), fp32 per row
+    // workspace: delta = rowsum(dO o O) and nlse = -LSE log2(e), fp32 per row
     float *delta, *nlse;
     int64_t s_o[3], s_do[3], s_dq[3], s_dk[3], s_dv[3];
 };
@@ -159,8 +158,7 @@ struct BwdWorkspace {
 };
 BwdWorkspace bwd_workspace(int64_t B, int64_t H, int64_t N, int64_t D);
 hipError_t launch_attn_bwd_bf16(const BwdArgs &a, hipStream_t st);
-// fp32 inputs (attn_bwd_f32.hip): the same gradients in fp32 arithmetic, the
-// workspace's second array holding -LSE log2(e) for them.
+// fp32 inputs (attn_bwd_f32.hip): the same gradients in fp32 arithmetic.
 hipError_t launch_attn_bwd_f32(const BwdArgs &a, hipStream_t st);
 
 // SALAD linear branch (attn_linear_bf16.hip).
