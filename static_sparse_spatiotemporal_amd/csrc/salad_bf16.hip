@@ -305,20 +305,32 @@ void k_salad_combine(CombineArgs a)
         f32x4 bias4 = {0.f, 0.f, 0.f, 0.f};
         if (a.bias != nullptr && col_ok)
             bias4 = *(const f32x4 *)(a.bias + cglob);
+        // The O_s pieces and gate values of all 16 rows are loaded before
+        // any is used (addresses clamped into the tensors, stores masked),
+        // so that their latencies overlap instead of adding up row by row.
+        const int hpc = col_ok ? hp : 0, epc = col_ok ? ep : 0;
+        bf16x4 o4[16];
+        float gv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            uint32_t R = (uint32_t)(m0 + wm * G::TMW + tt * 32 + 2 * i + hh);
+            R = R < (uint32_t)a.M ? R : (uint32_t)a.M - 1u;
+            const uint32_t bb = R / (uint32_t)a.N, nn = R - bb * (uint32_t)a.N;
+            gv[i] = a.gate[bb];
+            o4[i] = *(const bf16x4 *)(a.os + (int64_t)bb * a.s_os[0] + hpc * a.s_os[1] + (int64_t)nn * a.s_os[2] +
+                                      epc);
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int row = 2 * i + hh;
             const f32x4 v = *(const f32x4 LDS_AS *)(st + row * 512 + ((chunk ^ (row & 31)) << 4));
             const uint32_t R = (uint32_t)(m0 + wm * G::TMW + tt * 32 + row);
+            f32x4 res;
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                res[x] = (float)o4[i][x] + gv[i] * (v[x] + bias4[x]);
             if (R < (uint32_t)a.M && col_ok) {
                 const uint32_t bb = R / (uint32_t)a.N, nn = R - bb * (uint32_t)a.N;
-                const float gv = a.gate[bb];
-                const bf16x4 o4 = *(const bf16x4 *)(a.os + (int64_t)bb * a.s_os[0] + hp * a.s_os[1] +
-                                                    (int64_t)nn * a.s_os[2] + ep);
-                f32x4 res;
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    res[x] = (float)o4[x] + gv * (v[x] + bias4[x]);
                 *(bf16x4 *)(a.out + (int64_t)bb * a.s_out[0] + hp * a.s_out[1] + (int64_t)nn * a.s_out[2] + ep) =
                     __builtin_convertvector(res, bf16x4);
             }
