@@ -179,6 +179,33 @@ def test_ragged_and_degenerate_full_parity(tra, case):
         assert torch.equal(out, v)
 
 
+RAMP = [
+    # (kind, f, s, granularity, extra, D, dtype): head 0 ramps up, head 1 down
+    ("radial", 10, 200, "element", {}, 64, "bf16"),
+    ("radial", 10, 200, "element", {}, 128, "bf16"),
+    ("radial", 10, 200, "element", {}, 64, "f32"),
+    ("radial", 10, 200, "element", {}, 128, "f32"),
+    ("radial", 12, 256, "block_eq4", {}, 128, "bf16"),
+    ("radial", 12, 256, "block_eq4", {}, 64, "bf16"),
+    ("radial", 7, 100, "block_any", dict(sink_frames=1), 64, "bf16"),
+    ("swa", 9, 128, "element", dict(window=3, sink_frames=1), 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", RAMP, ids=lambda c: f"{c[0]}-f{c[1]}-s{c[2]}-{c[3]}-D{c[5]}-{c[6]}")
+def test_growing_and_shrinking_scores(tra, case):
+    """Scores that ramp by about 240 log2 units along each row: the running
+    row maximum moves by far more than the rescale threshold between key
+    blocks, up on one head and down on the other, and an exponent taken
+    against a stale maximum would overflow fp32."""
+    kind, f, s, gran, extra, D, dt = case
+    w = workloads.Workload(f"ramp_{kind}_f{f}_s{s}", kind, gran, f, s, 1, 2, D, dt, seed=515 + f + D, **extra)
+    q, k, v = workloads.make_ramp_qkv(w, span=240.0, device="cuda")
+    eo, el, out, lse = run_and_compare(tra, w, q, k, v)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    assert eo <= TOL_O[dt] and el <= 1
+
+
 def test_strided_views(tra):
     """Q, K, V as [B, H, n, D] views of [B, n, H, D] storage (the layout a fused
     QKV projection produces), output into a strided view as well."""

@@ -30,8 +30,8 @@ def frames_qkv(B, H, f, s, D, seed):
     return workloads.make_qkv(w, device="cuda")  # [B, H, f * s, D]
 
 
-def check_stream(tra, B, H, s, D, window, nframes, seed, check_frames=None, rows_per_frame=None):
-    q, k, v = frames_qkv(B, H, nframes, s, D, seed)
+def check_stream(tra, B, H, s, D, window, nframes, seed, check_frames=None, rows_per_frame=None, qkv=None):
+    q, k, v = frames_qkv(B, H, nframes, s, D, seed) if qkv is None else qkv
     cache = tra.KVCache(B, H, s, D, window)
     errs = []
     for i in range(nframes):
@@ -75,6 +75,17 @@ def test_stream_odd_query_blocks(tra):
     """384 tokens per frame: three query blocks, so the second pair of query
     blocks holds one block."""
     check_stream(tra, B=1, H=2, s=384, D=128, window=2, nframes=4, seed=710)
+
+
+def test_stream_growing_and_shrinking_scores(tra):
+    """Scores ramping by about 480 log2 units along the sequence (up on head
+    0, down on head 1), about 240 within each row's three-frame window: the
+    maxima of the key splits the merge combines are over 100 log2 units
+    apart, so a merge that took exponents against the wrong maximum would
+    overflow or flush to zero."""
+    w = workloads.Workload("stream_ramp", "swa", "element", 6, 128, 1, 2, 128, "bf16", seed=909)
+    qkv = workloads.make_ramp_qkv(w, span=480.0, device="cuda")
+    check_stream(tra, 1, 2, 128, 128, 3, 6, 909, qkv=qkv)
 
 
 def test_stream_repeat_is_bitwise(tra):

@@ -103,6 +103,36 @@ def make_qkv(w: Workload, device="cpu", seed: int | None = None, heads: int | No
     return tuple(out)
 
 
+def make_ramp_qkv(w: Workload, span: float, device="cpu", seed: int | None = None):
+    """Seeded Q, K, V of shape [B, H, n, D] whose scores ramp along the key
+    index, so that a query row's largest score keeps growing (even heads) or
+    keeps shrinking (odd heads) from one key block to the next.
+
+    With t_j spaced evenly over [-A, A] along the n keys (A chosen so that
+    q . k / sqrt(D) * log2(e) moves by about `span` over the sequence for
+    q near the all-ones vector): Q = 1 + 0.1 N(0, 1), K[j] = +/- t_j +
+    0.5 N(0, 1) (+ on even heads), V = 0.5 N(0, 1); one generator on
+    `device`, drawn in the order Q, K, V, then rounded to bf16 for bf16
+    workloads.  A span well above 128 makes an exponent taken against a
+    stale row maximum overflow fp32.
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed if seed is None else seed)
+    shape = (w.B, w.H, w.n, w.D)
+    half = span / (math.log2(math.e) * math.sqrt(w.D)) / 2
+    t = torch.linspace(-half, half, w.n, dtype=torch.float32, device=device)
+    sign = torch.tensor([1.0 if h % 2 == 0 else -1.0 for h in range(w.H)], dtype=torch.float32,
+                        device=device)
+    q = 1.0 + 0.1 * torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    k = sign[None, :, None, None] * t[None, None, :, None] + \
+        0.5 * torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    v = 0.5 * torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    out = (q, k, v)
+    if w.dtype == "bf16":
+        out = tuple(x.to(torch.bfloat16) for x in out)
+    return out
+
+
 def make_salad_inputs(B: int, H: int, N: int, D: int, seed: int, device="cpu"):
     """Seeded synthetic inputs of the SALAD gate and output, as a dict.
 
