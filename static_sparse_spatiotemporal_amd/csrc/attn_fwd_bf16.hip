@@ -35,7 +35,10 @@
 //   - operand fragments are read one step ahead of the MFMAs that use them;
 //   - the accumulator is rescaled only when some row's maximum grows by more
 //     than 2^8 (wave-uniform test); otherwise the stale maximum is kept, which
-//     leaves probabilities <= 2^8 and the result exact up to rounding;
+//     leaves probabilities <= 2^8 and the result exact up to rounding.  At
+//     D = 64 the tile maximum is not even looked for once every row has one:
+//     the exponentials are taken against the maximum in use and redone after
+//     a rescale only when a lane's sum of them passes 2^32;
 //   - partly kept tiles get their element bitmask applied to the scores; the
 //     waves of a query block that does not keep a tile of the union skip it;
 //   - workgroups are persistent and pop items from per-XCD queues of chunks
@@ -262,42 +265,64 @@ void attn_fwd_bf16(AttnArgs a)
                     }
             }
             // ---- streaming softmax (base 2) ----
-            float mx = kNegInf;
-#pragma unroll
-            for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    mx = fmaxf(mx, s[kb4][i]);
-            const float mt = lane_pair_max(mx) + muse;
-            if (__builtin_amdgcn_ballot_w64(mt > m + tau)) {
-                const float mn = fmaxf(m, mt);
-                const float alpha = __builtin_amdgcn_exp2f((m - (mn == kNegInf ? 0.f : mn)) * c2);
-#pragma unroll
-                for (int db = 0; db < G::NDB; ++db)
-                    o[db] *= alpha;
-                l *= alpha;
-                m = mn;
-                // re-base this tile's scores on the new maximum
-                const float mu = m == kNegInf ? 0.f : m;
-                const float dm = mu - muse;
-                muse = mu;
+            // At D = 64, once every row of the wave has a finite maximum, a
+            // tile's probabilities are first taken against the maximum in
+            // use without looking for the tile's own maximum; only if some
+            // lane's sum of them passes 2^32 (a score more than 26 above the
+            // maximum, in log2 units) is the maximum taken and the tile's
+            // exponentials redone.  Probabilities up to 2^32 leave bf16 and
+            // the fp32 sums far from overflow, and the result is the same
+            // up to rounding.  (At D = 128 the second exponential loop does
+            // not fit the registers.)
+            const bool lazy = D == 64 && !__builtin_amdgcn_ballot_w64(m == kNegInf);
+            auto take_max = [&]() {
+                float mx = kNegInf;
 #pragma unroll
                 for (int kb4 = 0; kb4 < 4; ++kb4)
-                    s[kb4] -= dm;
-            }
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        mx = fmaxf(mx, s[kb4][i]);
+                const float mt = lane_pair_max(mx) + muse;
+                if (__builtin_amdgcn_ballot_w64(mt > m + tau)) {
+                    const float mn = fmaxf(m, mt);
+                    const float alpha = __builtin_amdgcn_exp2f((m - (mn == kNegInf ? 0.f : mn)) * c2);
+#pragma unroll
+                    for (int db = 0; db < G::NDB; ++db)
+                        o[db] *= alpha;
+                    l *= alpha;
+                    m = mn;
+                    // re-base this tile's scores on the new maximum
+                    const float mu = m == kNegInf ? 0.f : m;
+                    const float dm = mu - muse;
+                    muse = mu;
+#pragma unroll
+                    for (int kb4 = 0; kb4 < 4; ++kb4)
+                        s[kb4] -= dm;
+                }
+            };
             // fp32 row sums (the LSE output keeps fp32 accuracy); the P V
             // product uses the probabilities rounded to bf16.
             bf16x8 pf[8];
-            float ls[2] = {0.f, 0.f};
+            float ls[2];
+            auto exps = [&]() {
+                ls[0] = ls[1] = 0.f;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                f32x8 pv;
+                for (int t = 0; t < 8; ++t) {
+                    f32x8 pv;
 #pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    pv[x] = __builtin_amdgcn_exp2f(s[t >> 1][8 * (t & 1) + x] * c2);
-                    ls[x & 1] += pv[x];
+                    for (int x = 0; x < 8; ++x) {
+                        pv[x] = __builtin_amdgcn_exp2f(s[t >> 1][8 * (t & 1) + x] * c2);
+                        ls[x & 1] += pv[x];
+                    }
+                    pf[t] = __builtin_convertvector(pv, bf16x8);
                 }
-                pf[t] = __builtin_convertvector(pv, bf16x8);
+            };
+            if (!lazy)
+                take_max();
+            exps();
+            if (lazy && __builtin_amdgcn_ballot_w64(!(ls[0] + ls[1] <= 0x1p32f))) {
+                take_max();
+                exps();
             }
             l += ls[0] + ls[1];
 
