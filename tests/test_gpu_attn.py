@@ -206,6 +206,18 @@ def test_growing_and_shrinking_scores(tra, case):
     assert eo <= TOL_O[dt] and el <= 1
 
 
+@pytest.mark.parametrize("D,dt", [(64, "bf16"), (128, "bf16"), (64, "f32"), (128, "f32")])
+def test_scores_far_from_zero(tra, D, dt):
+    """Every score about 150 log2 units above 0, spread over a few units:
+    the LSE is about 104 and the probabilities are taken against a maximum
+    of that size from the first tile on."""
+    w = workloads.Workload(f"offset_radial_f10_s200_D{D}", "radial", "element", 10, 200, 1, 2, D, dt, seed=717 + D)
+    q, k, v = workloads.make_ramp_qkv(w, span=0.0, device="cuda", offset=150.0)
+    eo, el, out, lse = run_and_compare(tra, w, q, k, v)
+    assert float(lse.min()) > 90.0
+    assert eo <= TOL_O[dt] and el <= 1
+
+
 def test_strided_views(tra):
     """Q, K, V as [B, H, n, D] views of [B, n, H, D] storage (the layout a fused
     QKV projection produces), output into a strided view as well."""

@@ -35,8 +35,8 @@ def spec_of(w):
                            r_t=w.r_t, r_s=w.r_s, window=w.window, sink_frames=w.sink_frames)
 
 
-def run_bwd(tra, w, mask):
-    q, k, v = workloads.make_qkv(w, device="cuda")
+def run_bwd(tra, w, mask, qkv=None):
+    q, k, v = workloads.make_qkv(w, device="cuda") if qkv is None else qkv
     do = make_dout(w)
     out, lse = tra.sparse_attn_fwd(q, k, v, mask)
     dq, dk, dv = tra.sparse_attn_bwd(q, k, v, out, lse, do, mask)
@@ -58,10 +58,13 @@ def tol(ref, dtype="bf16"):
     return TOL[dtype][0] * max(1.0, float(np.abs(ref).max()))
 
 
-def compare(tra, w, q_rows=None, k_rows=None, tag=""):
+def compare(tra, w, q_rows=None, k_rows=None, tag="", qkv=None, rms=None):
+    """Gradients of `w` (inputs from make_qkv, or `qkv`) against the oracle
+    on the given rows (None = all).  `rms` maps a gradient name to its
+    relative-RMS limit (default: TOL for every gradient; None: not checked)."""
     print(f"[bwd] {w.name}{tag} B={w.B} H={w.H} n={w.n} D={w.D}", flush=True)
     mask = tra.build_mask(w.f, w.s, w.kind, **w.mask_kwargs())
-    (q, k, v, do), (dq, dk, dv) = run_bwd(tra, w, mask)
+    (q, k, v, do), (dq, dk, dv) = run_bwd(tra, w, mask, qkv=qkv)
     mask.free()
     spec = spec_of(w)
     bk = None
@@ -79,10 +82,11 @@ def compare(tra, w, q_rows=None, k_rows=None, tag=""):
         print(f"       {name}: max|err|={e:.3e} rel-rms={rel:.2e} max|ref|={np.abs(ref).max() if ref.size else 0:.3f}",
               flush=True)
         errs.append((name, e, tol(ref, w.dtype) if ref.size else 1.0))
-        if ref.size and float(np.abs(ref).max()) > 1e-3:
+        limit = TOL[w.dtype][1] if rms is None else rms.get(name)
+        if limit is not None and ref.size and float(np.abs(ref).max()) > 1e-3:
             # bf16: the rounding of the outputs and of P and dS gives about
             # 2.4e-3; a wrong term or sign would give O(1)
-            assert rel <= TOL[w.dtype][1], (name, rel)
+            assert rel <= limit, (name, rel)
     for name, e, t in errs:
         assert e <= t, (name, e, t)
     return (q, k, v, do), (dq, dk, dv)
@@ -113,6 +117,42 @@ def test_bwd_full_parity(tra, case):
         # one key per row: P = 1 and dP = delta = dO . V, so dS vanishes up to
         # the fp32 rounding of two sums of the same D products
         assert float(dq.float().abs().max()) <= 1e-4 and float(dk.float().abs().max()) <= 1e-4
+
+
+LARGE_SCORES = [
+    # (D, dtype, span, offset): scores ramping by about 240 log2 units along
+    # each row (up on head 0, down on head 1), or all about 150 log2 units
+    # above 0 with a spread of a few units
+    (64, "bf16", 240.0, 0.0),
+    (128, "bf16", 240.0, 0.0),
+    (64, "bf16", 0.0, 150.0),
+    (128, "bf16", 0.0, 150.0),
+    (64, "f32", 240.0, 0.0),
+    (128, "f32", 0.0, 150.0),
+]
+
+
+@pytest.mark.parametrize("case", LARGE_SCORES, ids=lambda c: f"D{c[0]}-{c[1]}-span{c[2]:g}-offset{c[3]:g}")
+def test_bwd_large_scores(tra, case):
+    """Scores far from 0 (ramped, or shifted by a common offset), where P is
+    formed as exp2(q.k scale log2(e) - LSE log2(e)) from two large terms.
+    Every gradient element must meet the usual bound.  The relative RMS of
+    dK and dV is held to 1e-2 (bf16) and 1e-4 (fp32: scores of about 10^3
+    raw units carry 2^-24 of that as absolute error, about 1e-5 relative on
+    each probability), and that of dQ is only printed: sum_j dS_j = 0, so
+    dQ = scale sum_j dS_j k_j cancels what the kept keys have in common,
+    and the bf16 rounding of dS (and of O in delta) leaves errors of the
+    order of 2^-9 times that common part against a small dQ (the fp32
+    kernel's rounding is amplified the same way).  Measured on MI355X: dQ
+    relative RMS 3.9e-2 to 7.2e-2 in bf16 and 1.8e-4 to 3.5e-4 in fp32, with
+    every element inside the bound; dK and dV 2.3e-3 (bf16) and 5e-6 to
+    6e-6 (fp32)."""
+    D, dt, span, offset = case
+    w = workloads.Workload(f"large_scores_radial_f10_s200_D{D}", "radial", "element", 10, 200, 1, 2, D, dt,
+                           seed=6100 + D + int(offset))
+    qkv = workloads.make_ramp_qkv(w, span, device="cuda", offset=offset)
+    lim = 1e-2 if dt == "bf16" else 1e-4
+    compare(tra, w, qkv=qkv, rms={"dK": lim, "dV": lim})
 
 
 F32_CASES = [

@@ -103,28 +103,31 @@ def make_qkv(w: Workload, device="cpu", seed: int | None = None, heads: int | No
     return tuple(out)
 
 
-def make_ramp_qkv(w: Workload, span: float, device="cpu", seed: int | None = None):
+def make_ramp_qkv(w: Workload, span: float, device="cpu", seed: int | None = None, offset: float = 0.0):
     """Seeded Q, K, V of shape [B, H, n, D] whose scores ramp along the key
     index, so that a query row's largest score keeps growing (even heads) or
     keeps shrinking (odd heads) from one key block to the next.
 
     With t_j spaced evenly over [-A, A] along the n keys (A chosen so that
     q . k / sqrt(D) * log2(e) moves by about `span` over the sequence for
-    q near the all-ones vector): Q = 1 + 0.1 N(0, 1), K[j] = +/- t_j +
-    0.5 N(0, 1) (+ on even heads), V = 0.5 N(0, 1); one generator on
+    q near the all-ones vector) and c the shift that raises every score by
+    about `offset` in the same units: Q = 1 + 0.1 N(0, 1), K[j] = c +/- t_j
+    + 0.5 N(0, 1) (+ on even heads), V = 0.5 N(0, 1); one generator on
     `device`, drawn in the order Q, K, V, then rounded to bf16 for bf16
     workloads.  A span well above 128 makes an exponent taken against a
-    stale row maximum overflow fp32.
+    stale row maximum overflow fp32; span 0 with a large offset gives rows
+    of nearly equal scores that are all far from 0.
     """
     g = torch.Generator(device=device)
     g.manual_seed(w.seed if seed is None else seed)
     shape = (w.B, w.H, w.n, w.D)
-    half = span / (math.log2(math.e) * math.sqrt(w.D)) / 2
+    unit = math.log2(math.e) * math.sqrt(w.D)   # score change, log2 units, per unit of t
+    half = span / unit / 2
     t = torch.linspace(-half, half, w.n, dtype=torch.float32, device=device)
     sign = torch.tensor([1.0 if h % 2 == 0 else -1.0 for h in range(w.H)], dtype=torch.float32,
                         device=device)
     q = 1.0 + 0.1 * torch.randn(shape, generator=g, device=device, dtype=torch.float32)
-    k = sign[None, :, None, None] * t[None, None, :, None] + \
+    k = (offset / unit + sign[None, :, None, None] * t[None, None, :, None]) + \
         0.5 * torch.randn(shape, generator=g, device=device, dtype=torch.float32)
     v = 0.5 * torch.randn(shape, generator=g, device=device, dtype=torch.float32)
     out = (q, k, v)
