@@ -415,6 +415,37 @@ def sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     return grads
 
 
+class _SparseAttention(torch.autograd.Function):
+    """sparse_attn_fwd as an autograd node: the backward calls
+    sparse_attn_bwd with the saved inputs, output and row log-sum-exp."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, mask, scale):
+        out, lse = sparse_attn_fwd(q, k, v, mask, scale=scale)
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.mask, ctx.scale = mask, scale
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse = ctx.saved_tensors
+        # the upstream gradient may be an expanded or strided view; the
+        # kernels read [B, H, N, D] views with unit stride in D
+        dq, dk, dv = sparse_attn_bwd(q, k, v, out, lse, dout.contiguous(), ctx.mask, scale=ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
+                     scale: float | None = None) -> torch.Tensor:
+    """Differentiable O = softmax((Q K^T + M) * scale) V: the forward and, when
+    autograd asks for them, the gradients of q, k and v, both through the
+    library's kernels (tra_sparse_attn_fwd, tra_sparse_attn_bwd; Radial
+    Attention page, section 6, trains through a block-sparse backward).
+    Same arguments as sparse_attn_fwd; `mask` must stay alive (not freed)
+    until the backward has run."""
+    return _SparseAttention.apply(q, k, v, mask, scale)
+
+
 def sparse_attn_bwd_workspace_bytes(B: int, H: int, n: int, D: int) -> int:
     return int(load_library().tra_sparse_attn_bwd_workspace_bytes(B, H, n, D))
 

@@ -41,6 +41,8 @@ def test_host_tensors_are_refused_before_any_call(no_lib):
     with pytest.raises(ValueError, match="HIP device"):
         tra.sparse_attn_fwd(q, q, q, m)
     with pytest.raises(ValueError, match="HIP device"):
+        tra.sparse_attention(q, q, q, m)
+    with pytest.raises(ValueError, match="HIP device"):
         tra.sparse_attn_bwd(q, q, q, q, _host(1, 2, 256, dtype=torch.float32), q, m)
     with pytest.raises(ValueError, match="HIP device"):
         tra.linear_attn_fwd(q, q, q)

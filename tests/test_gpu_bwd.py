@@ -311,3 +311,33 @@ def test_bwd_custom_scale(tra):
         rel = float(np.sqrt(((g - ref) ** 2).sum() / max((ref ** 2).sum(), 1e-30)))
         print(f"[bwd scale] {name}: max|err|={e:.3e} rel-rms={rel:.2e}", flush=True)
         assert e <= tol(ref) and rel <= 1e-2, (name, e, rel)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_autograd_matches_explicit_calls(tra, dt):
+    """sparse_attention under autograd returns the same output and the same
+    gradients, bit for bit, as sparse_attn_fwd followed by sparse_attn_bwd
+    with the upstream gradient autograd passes: a weighted sum of the output
+    (upstream gradient = the weights in the output's dtype), and a plain sum
+    (an expanded upstream gradient of ones, which the wrapper makes
+    contiguous).  The explicit calls are checked against the oracle above."""
+    w = workloads.Workload("autograd_radial_f10_s50", "radial", "element", 10, 50, 1, 2, 64, dt, seed=8080)
+    print(f"[bwd] autograd {w.name} {dt}", flush=True)
+    q, k, v = workloads.make_qkv(w, device="cuda")
+    mask = tra.build_mask(w.f, w.s, w.kind, **w.mask_kwargs())
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    weights = torch.randn(q.shape, generator=g, device="cuda")
+    ref_out, ref_lse = tra.sparse_attn_fwd(q, k, v, mask)
+    for name, loss_of, dout in (("weighted", lambda o: (o.float() * weights).sum(), weights.to(q.dtype)),
+                                ("sum", lambda o: o.sum(), torch.ones_like(q))):
+        qa, ka, va = (x.clone().requires_grad_(True) for x in (q, k, v))
+        out = tra.sparse_attention(qa, ka, va, mask)
+        loss_of(out).backward()
+        torch.cuda.synchronize()
+        dq, dk, dv = tra.sparse_attn_bwd(q, k, v, ref_out, ref_lse, dout, mask)
+        torch.cuda.synchronize()
+        assert torch.equal(out.detach(), ref_out), name
+        for got, ref, what in ((qa.grad, dq, "dQ"), (ka.grad, dk, "dK"), (va.grad, dv, "dV")):
+            assert got is not None and got.dtype == q.dtype and torch.equal(got, ref), (name, what)
+    mask.free()
