@@ -51,7 +51,7 @@ PairSchedule build_pairs(int nrows, int64_t s, const std::vector<int32_t> &ptr, 
         if (used[r])
             continue;
         int best = -1;
-        double bj = 0.5;
+        double bj = 0.0;
         for (int off : offs) {
             const int r2 = r + off;
             if (r2 >= nrows || used[r2])

@@ -30,10 +30,12 @@ std::vector<int32_t> chunk_order(const std::vector<int64_t> &weight, int chunk);
 // Pair schedule of a block mask given as CSR lists (row r keeps blocks
 // col[ptr[r]] .. in ascending order, each with an emask index, -1 = full):
 // greedy pairing of rows, in order, with the unpaired partner among r + 1
-// and r + s / 128 (same position in the next frame) that shares the most
-// blocks, if the Jaccard overlap exceeds 1/2; then the merged block list of
-// each pair with one emask index per member (kAbsent where the member does
-// not keep the block), and the chunk-wise heaviest-first pair order.
+// and r + s / 128 (same position in the next frame) of larger Jaccard
+// overlap, if the two share any block (a tile step that serves one member
+// of a pair costs what a step of an unpaired row costs, and a shared block
+// serves both, so any overlap pays); then the merged block list of each
+// pair with one emask index per member (kAbsent where the member does not
+// keep the block), and the chunk-wise heaviest-first pair order.
 struct PairSchedule {
     std::vector<int32_t> rows;   // [npairs][2] member rows (second -1: unpaired)
     std::vector<int32_t> ptr;    // [npairs + 1] offsets into col / em

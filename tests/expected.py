@@ -61,7 +61,7 @@ def pair_schedule(keep: np.ndarray, s: int):
     order; an unpaired row r takes, among the unpaired rows r + 1 and
     r + s / 128 (the latter when s is a multiple of 128 above 128), the one
     whose kept-block set has the larger Jaccard overlap with r's, the first
-    on ties, if that overlap exceeds 1/2 (two empty sets count as 1).  A pair
+    on ties, if that overlap is above 0 (two empty sets count as 1).  A pair
     loads the union of its two rows' blocks."""
     nr = keep.shape[0]
     offs = [1] + ([s // BLOCK] if s % BLOCK == 0 and s // BLOCK > 1 else [])
@@ -70,7 +70,7 @@ def pair_schedule(keep: np.ndarray, s: int):
     for r in range(nr):
         if used[r]:
             continue
-        best, bj = -1, 0.5
+        best, bj = -1, 0.0
         for off in offs:
             r2 = r + off
             if r2 >= nr or used[r2]:
