@@ -36,7 +36,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 def kernel_source_digest() -> str:
     import hashlib
     h = hashlib.sha256()
-    for fn in ("attn_fwd_bf16.hip", "attn_common.h", "tra_internal.h"):
+    for fn in ("attn_fwd_bf16.hip", "attn_common.h", "tra_internal.h", "tra_sched.h", "tra_sched.cpp"):
         with open(os.path.join(ROOT, "static_sparse_spatiotemporal_amd", "csrc", fn), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
