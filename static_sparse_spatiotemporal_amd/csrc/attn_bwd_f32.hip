@@ -5,17 +5,19 @@
 //   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - delta),
 //   dK = scale dS^T Q,   dQ = scale dS K.
 // The fp32 workloads are small, so these kernels aim at plain, exact fp32
-// work rather than matrix cores: a row is split over 16 lanes, each lane
-// holding D / 16 of its columns; dot products are finished with lane
-// shuffles.  Three kernels, no atomics (deterministic):
+// work rather than matrix cores: a row is split over 16 lanes (one DPP row
+// of the wave), each lane holding D / 16 of its columns; dot products are
+// finished with DPP row rotations.  Three kernels, no atomics
+// (deterministic):
 //   k_bwd_f32_prep  per row: delta and -LSE log2(e);
 //   k_bwd_f32_dq    per 16 query rows of a query block: every kept key of
-//                   the block's CSR row, K and V staged in LDS 32 keys at a
-//                   time;
+//                   the block's CSR row, K and V staged in LDS 128 keys (D =
+//                   64) or 64 keys (D = 128) at a time, the row's element
+//                   mask read once per block;
 //   k_bwd_f32_dkdv  per 16 key rows of a key block: every query block that
 //                   keeps the key block (the mask's schedule over key
-//                   blocks), Q, dO, -LSE log2(e) and delta staged 32 queries
-//                   at a time.
+//                   blocks), Q, dO, -LSE log2(e), delta and the element-mask
+//                   word of each query staged 128 or 64 queries at a time.
 #include "attn_common.h"
 
 namespace tra {
@@ -24,24 +26,24 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kLanes = 16;               // lanes per row
 constexpr int kRows = 256 / kLanes;      // rows per workgroup
-constexpr int kSub = 32;                 // staged rows per step
+// staged rows per step: 64 KB of LDS for the two staged operands
+template <int D>
+constexpr int kSubOf() { return D == 64 ? 128 : 64; }
 
-// Sum over the 16 lanes of a row (the same value on all of them).
+// Sum over the 16 lanes of a row, which are one DPP row of the wave (lanes
+// 16 k .. 16 k + 15): four additions of the value rotated within the row by
+// 8, 4, 2 and 1 lanes (row_ror), each a single VALU instruction, where a
+// lane shuffle would go through the LDS crossbar.  Every lane adds the same
+// pairs of partial sums, in one order or the other, so all 16 get the same
+// bits.
+template <int R>
+__device__ inline float row_ror_add(float v)
+{
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + R, 0xf, 0xf, false));
+}
 __device__ inline float row_sum(float v)
 {
-#pragma unroll
-    for (int off = 1; off < kLanes; off <<= 1)
-        v += __shfl_xor(v, off, kLanes);
-    return v;
-}
-
-// Element-mask bit of (query row r of block, key column c of block); a full
-// block (em < 0) keeps everything.
-__device__ inline bool kept(const uint32_t *emask, int em, int r, int c)
-{
-    if (em < 0)
-        return true;
-    return (emask[((size_t)em * kBlock + r) * 4 + (c >> 5)] >> (c & 31)) & 1u;
+    return row_ror_add<1>(row_ror_add<2>(row_ror_add<4>(row_ror_add<8>(v))));
 }
 
 template <int D>
@@ -74,6 +76,7 @@ template <int D>
 __global__ __launch_bounds__(256) void k_bwd_f32_dq(BwdArgs a)
 {
     constexpr int PER = D / kLanes;
+    constexpr int kSub = kSubOf<D>();
     __shared__ float sK[kSub][D];
     __shared__ float sV[kSub][D];
     const AttnArgs &f = a.f;
@@ -105,16 +108,22 @@ __global__ __launch_bounds__(256) void k_bwd_f32_dq(BwdArgs a)
     for (int e = e0; e < e1; ++e) {
         const int kb = f.mask.col_idx[e];
         const int em = f.mask.emask_idx[e];
+        // this row's element mask over the block's 128 keys, read once
+        uint4 mw = make_uint4(~0u, ~0u, ~0u, ~0u);
+        if (em >= 0)
+            mw = ((const uint4 *)f.mask.emask)[(size_t)em * kBlock + r];
+        const uint32_t words[4] = {mw.x, mw.y, mw.z, mw.w};
         for (int s0 = 0; s0 < kBlock; s0 += kSub) {
             const int key0 = kb * kBlock + s0;
             __syncthreads();
-            for (int c = tid; c < kSub * D; c += 256) {
-                const int kr = c / D, col = c - kr * D;
+            for (int c = tid; c < kSub * D / 4; c += 256) {
+                const int kr = c / (D / 4), col = 4 * (c - kr * (D / 4));
                 const int key = key0 + kr < N ? key0 + kr : N - 1;
-                sK[kr][col] = Kp[(int64_t)key * f.sk[2] + col];
-                sV[kr][col] = Vp[(int64_t)key * f.sv[2] + col];
+                *(float4 *)&sK[kr][col] = *(const float4 *)(Kp + (int64_t)key * f.sk[2] + col);
+                *(float4 *)&sV[kr][col] = *(const float4 *)(Vp + (int64_t)key * f.sv[2] + col);
             }
             __syncthreads();
+#pragma unroll 2
             for (int j = 0; j < kSub; ++j) {
                 float s = 0.f, dp = 0.f;
 #pragma unroll
@@ -124,7 +133,8 @@ __global__ __launch_bounds__(256) void k_bwd_f32_dq(BwdArgs a)
                 }
                 s = row_sum(s);
                 dp = row_sum(dp);
-                const bool keep = live && key0 + j < N && kept(f.mask.emask, em, r, s0 + j);
+                const int jb = s0 + j;
+                const bool keep = live && key0 + j < N && ((words[jb >> 5] >> (jb & 31)) & 1u);
                 const float p = keep ? exp2f(s + nl) : 0.f;
                 const float ds = p * (dp - dl);
 #pragma unroll
@@ -146,9 +156,11 @@ template <int D>
 __global__ __launch_bounds__(256) void k_bwd_f32_dkdv(BwdArgs a)
 {
     constexpr int PER = D / kLanes;
+    constexpr int kSub = kSubOf<D>();
     __shared__ float sQ[kSub][D];
     __shared__ float sG[kSub][D];
     __shared__ float sL[kSub], sD[kSub];
+    __shared__ uint32_t sM[kSub];  // mask word of each staged query over this workgroup's 16 keys
     const AttnArgs &f = a.f;
     const int tid = threadIdx.x, x = tid % kLanes, rr = tid / kLanes;
     const int slices = kBlock / kRows;
@@ -188,18 +200,21 @@ __global__ __launch_bounds__(256) void k_bwd_f32_dkdv(BwdArgs a)
         for (int s0 = 0; s0 < kBlock; s0 += kSub) {
             const int q0 = qb * kBlock + s0;
             __syncthreads();
-            for (int i = tid; i < kSub * D; i += 256) {
-                const int qr = i / D, col = i - qr * D;
+            for (int i = tid; i < kSub * D / 4; i += 256) {
+                const int qr = i / (D / 4), col = 4 * (i - qr * (D / 4));
                 const int q = q0 + qr < N ? q0 + qr : N - 1;
-                sQ[qr][col] = Qp[(int64_t)q * f.sq[2] + col];
-                sG[qr][col] = Gp[(int64_t)q * a.s_do[2] + col];
+                *(float4 *)&sQ[qr][col] = *(const float4 *)(Qp + (int64_t)q * f.sq[2] + col);
+                *(float4 *)&sG[qr][col] = *(const float4 *)(Gp + (int64_t)q * a.s_do[2] + col);
             }
             if (tid < kSub) {
                 const int q = q0 + tid < N ? q0 + tid : N - 1;
                 sL[tid] = Lp[q];
                 sD[tid] = Dp[q];
+                // the 16 key columns of this workgroup lie in one 32-column word
+                sM[tid] = em >= 0 ? f.mask.emask[((size_t)em * kBlock + s0 + tid) * 4 + ((slice * kRows) >> 5)] : ~0u;
             }
             __syncthreads();
+#pragma unroll 2
             for (int i = 0; i < kSub; ++i) {
                 float s = 0.f, dp = 0.f;
 #pragma unroll
@@ -209,7 +224,7 @@ __global__ __launch_bounds__(256) void k_bwd_f32_dkdv(BwdArgs a)
                 }
                 s = row_sum(s);
                 dp = row_sum(dp);
-                const bool keep = live && q0 + i < N && kept(f.mask.emask, em, s0 + i, c);
+                const bool keep = live && q0 + i < N && ((sM[i] >> (c & 31)) & 1u);
                 const float p = keep ? exp2f(s * c2 + sL[i]) : 0.f;
                 const float ds = p * (dp - sD[i]);
 #pragma unroll
