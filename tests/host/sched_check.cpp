@@ -6,6 +6,9 @@
 // What is checked, for each mask given as CSR lists (sorted columns, one
 // emask index each):
 //   - jaccard agrees with a set computation;
+//   - build_pairs pairs exactly the rows its rule names (replayed here on
+//     sets: rows in order, partner r + 1 or r + s / 128 of larger Jaccard
+//     overlap, first on ties, if above 0);
 //   - chunk_order keeps each chunk's items and sorts them by decreasing
 //     weight, ties in order;
 //   - build_pairs covers every row exactly once, pairs a row only with
@@ -178,6 +181,49 @@ void check_pairs(const Csr &m, int64_t s, const char *what)
     }
     for (int r = 0; r < m.nrows; ++r)
         CHECK(seen[r] == 1, "%s: row %d in %d pairs", what, r, seen[r]);
+    // the pairing rule, replayed with sets: rows in order; an unpaired row
+    // takes, among the unpaired rows r + 1 and r + step, the one of larger
+    // Jaccard overlap (the first on ties) if that overlap is above 0
+    {
+        std::vector<std::set<int32_t>> sets(m.nrows);
+        for (int r = 0; r < m.nrows; ++r)
+            for (int32_t e = m.ptr[r]; e < m.ptr[r + 1]; ++e)
+                sets[r].insert(m.col[e]);
+        auto jac = [&](int a, int b) {
+            std::vector<int32_t> inter, uni;
+            std::set_intersection(sets[a].begin(), sets[a].end(), sets[b].begin(), sets[b].end(),
+                                  std::back_inserter(inter));
+            std::set_union(sets[a].begin(), sets[a].end(), sets[b].begin(), sets[b].end(), std::back_inserter(uni));
+            return uni.empty() ? 1.0 : (double)inter.size() / (double)uni.size();
+        };
+        std::vector<char> used(m.nrows, 0);
+        std::vector<std::pair<int, int>> want;
+        for (int r = 0; r < m.nrows; ++r) {
+            if (used[r])
+                continue;
+            int best = -1;
+            double bj = 0.0;
+            std::vector<int> offs = {1};
+            if (step > 1)
+                offs.push_back(step);
+            for (int off : offs) {
+                const int r2 = r + off;
+                if (r2 < m.nrows && !used[r2] && jac(r, r2) > bj) {
+                    bj = jac(r, r2);
+                    best = r2;
+                }
+            }
+            used[r] = 1;
+            if (best >= 0)
+                used[best] = 1;
+            want.push_back({r, best});
+        }
+        CHECK((int)want.size() == np, "%s: %d pairs, the rule gives %d", what, np, (int)want.size());
+        for (int p = 0; p < np; ++p)
+            CHECK(ps.rows[2 * p] == want[p].first && ps.rows[2 * p + 1] == want[p].second,
+                  "%s: pair %d = (%d, %d), the rule gives (%d, %d)", what, p, ps.rows[2 * p], ps.rows[2 * p + 1],
+                  want[p].first, want[p].second);
+    }
     // chunk-wise heaviest first
     std::vector<int64_t> w(np);
     for (int p = 0; p < np; ++p)
