@@ -1,18 +1,19 @@
 """Host code under AddressSanitizer and UndefinedBehaviorSanitizer.
 
-Two drivers under tests/host/ are built with gcc/g++ and -fsanitize=address,
-undefined (no GPU code involved) and run in a child process:
+Two check programs under tests/host/ are built with gcc/g++ and
+-fsanitize=address,undefined (no GPU code involved) and run in a child
+process:
 
 * sched_check: the schedule builders of the library's host side
   (csrc/tra_sched.cpp: Jaccard pairing, merged block lists, chunk orders,
   CSR transpose) on seeded random and banded block masks, against set
-  computations;
+  computations and a replay of the pairing rule;
 * oracle_check: every entry point of the C oracle on small inputs, against
   element-by-element agreement of its mask functions and closed forms of
   its attention, gradient, linear-branch and SALAD results.
 
 Any out-of-bounds access, use after free, leak or undefined operation ends
-the driver with an error, as does a failed check.
+the check program with an error, as does a failed check.
 """
 import os
 import shutil
