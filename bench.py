@@ -202,7 +202,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1",
                           "gpus": args.gpus}))
         sys.exit(2)
 
@@ -337,7 +337,7 @@ def main():
         extra.update({"bwd_ms": round(bwd_ms, 3),
                       # 5 products per kept block (S, dP, dV, dK, dQ) is the usual accounting
                       "bwd_tflops_5gemm": round(2.5 * flops_blocks / (bwd_ms * 1e-3) / 1e12, 2),
-                      # this build recomputes S and dP for dQ: 7 products are executed
+                      # the backward recomputes S and dP for dQ: 7 products are executed
                       "bwd_mfma_tflops_7gemm": round(3.5 * flops_blocks / (bwd_ms * 1e-3) / 1e12, 2),
                       "bwd_pct_bf16_peak_7gemm": round(100 * 3.5 * flops_blocks / (bwd_ms * 1e-3) / 1e12
                                                        / BF16_PEAK_TFLOPS, 2)})

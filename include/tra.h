@@ -63,7 +63,7 @@ extern "C" {
 typedef enum {
     TRA_OK = 0,
     TRA_ERR_INVALID = -1,     /* null pointer, value out of range           */
-    TRA_ERR_UNSUPPORTED = -2, /* valid request this build does not handle   */
+    TRA_ERR_UNSUPPORTED = -2, /* valid request the library does not handle */
     TRA_ERR_SHAPE = -3,       /* tensor shapes disagree with each other/mask */
     TRA_ERR_OOM = -4,         /* device allocation failed                   */
     TRA_ERR_HIP = -5          /* other HIP runtime failure                  */
@@ -146,7 +146,7 @@ typedef struct {
  * block row/column is cut at n and every kept block that reaches past n
  * carries an element bitmask that drops the missing keys.
  *
- * Runs the mask-builder kernels on `hip_stream` and waits for them (the build
+ * Runs the mask-builder kernels on `hip_stream` and waits for them (the mask build
  * is synchronous; it is meant to run once per (f, s, kind, params)).  On
  * success *out owns device memory until tra_mask_free.  On failure *out is
  * NULL.  Errors: TRA_ERR_INVALID (null out/params, f or s < 1, unknown kind
