@@ -9,25 +9,29 @@ namespace {
 
 // Keys of a row split over 16 lanes: a workgroup of 256 threads takes 16
 // rows of a query block; lane x of a row handles keys x, x + 16, .. of every
-// kept block (K and V staged in LDS with a one-float pad per row, KH keys
-// per pass), keeping its own running maximum, denominator and output; the
+// kept block (K and V staged in LDS, rows padded to D + 4 floats and read
+// as float4, KH keys per pass), keeping its own running maximum, denominator
+// and output; the
 // 16 partial softmax states of a row are merged at the end (max, rescale,
 // add) with lane shuffles.  At D = 64 the scaled query row is held in
 // registers and whole blocks are staged; at D = 128 the query row is read
 // from LDS (the output alone takes 128 registers) and blocks are staged in
-// 64-key halves (66 KB of LDS).
+// 64-key halves (74 KB of LDS; 68 KB at D = 64).
 constexpr int kSplitLanes = 16;
 constexpr int kSplitRows = 256 / kSplitLanes;
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_f32_split(AttnArgs a)
 {
-    constexpr int DP = D + 1;
+    // Rows padded to D + 4 floats: 16-byte aligned for float4 reads, and the
+    // 16 lanes of a row, reading 16 consecutive keys at one column, hit 16
+    // distinct 4-bank groups.
+    constexpr int DP = D + 4;
     constexpr int KH = D == 64 ? kBlock : 64;  // keys staged per pass
     constexpr bool QLDS = D > 64;
-    __shared__ float sK[KH * DP];
-    __shared__ float sV[KH * DP];
-    __shared__ float sQ[QLDS ? kSplitRows * DP : 1];
+    __shared__ __attribute__((aligned(16))) float sK[KH * DP];
+    __shared__ __attribute__((aligned(16))) float sV[KH * DP];
+    __shared__ __attribute__((aligned(16))) float sQ[QLDS ? kSplitRows * DP : 4];
     const int tid = threadIdx.x;
     const int x = tid & (kSplitLanes - 1), rr = tid / kSplitLanes;
     const int per_bh = a.mask.nqb * (kBlock / kSplitRows);
@@ -88,9 +92,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_split(AttnArgs a)
                     kv = *(const float4 *)(Kp + (int64_t)key * a.sk[2] + col);
                     vv = *(const float4 *)(Vp + (int64_t)key * a.sv[2] + col);
                 }
-                float *dk = sK + row * DP + col, *dv = sV + row * DP + col;
-                dk[0] = kv.x; dk[1] = kv.y; dk[2] = kv.z; dk[3] = kv.w;
-                dv[0] = vv.x; dv[1] = vv.y; dv[2] = vv.z; dv[3] = vv.w;
+                *(float4 *)(sK + row * DP + col) = kv;
+                *(float4 *)(sV + row * DP + col) = vv;
             }
             __syncthreads();
 #pragma unroll 2
@@ -98,11 +101,18 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_split(AttnArgs a)
                 const int jb = h0 + j;  // key within the block
                 if (!((words[jb >> 5] >> (jb & 31)) & 1u))
                     continue;
-                const float *kr = sK + j * DP;
-                float sc = 0.f;
+                const float4 *kr = (const float4 *)(sK + j * DP);
+                float s4[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums
 #pragma unroll
-                for (int d = 0; d < D; ++d)
-                    sc = fmaf(QLDS ? qrow[d] : qv[d], kr[d], sc);
+                for (int d4 = 0; d4 < D / 4; ++d4) {
+                    const float4 kk = kr[d4];
+                    const int d = 4 * d4;
+                    s4[0] = fmaf(QLDS ? qrow[d] : qv[d], kk.x, s4[0]);
+                    s4[1] = fmaf(QLDS ? qrow[d + 1] : qv[d + 1], kk.y, s4[1]);
+                    s4[2] = fmaf(QLDS ? qrow[d + 2] : qv[d + 2], kk.z, s4[2]);
+                    s4[3] = fmaf(QLDS ? qrow[d + 3] : qv[d + 3], kk.w, s4[3]);
+                }
+                const float sc = (s4[0] + s4[1]) + (s4[2] + s4[3]);
                 if (sc > m) {
                     const float alpha = __builtin_amdgcn_exp2f(m - sc);  // m = -inf gives 0
                     l *= alpha;
@@ -113,10 +123,15 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_split(AttnArgs a)
                 }
                 const float p = __builtin_amdgcn_exp2f(sc - m);
                 l += p;
-                const float *vr = sV + j * DP;
+                const float4 *vr = (const float4 *)(sV + j * DP);
 #pragma unroll
-                for (int d = 0; d < D; ++d)
-                    o[d] = fmaf(p, vr[d], o[d]);
+                for (int d4 = 0; d4 < D / 4; ++d4) {
+                    const float4 vv = vr[d4];
+                    o[4 * d4] = fmaf(p, vv.x, o[4 * d4]);
+                    o[4 * d4 + 1] = fmaf(p, vv.y, o[4 * d4 + 1]);
+                    o[4 * d4 + 2] = fmaf(p, vv.z, o[4 * d4 + 2]);
+                    o[4 * d4 + 3] = fmaf(p, vv.w, o[4 * d4 + 3]);
+                }
             }
         }
     }
