@@ -39,7 +39,10 @@ __device__ inline float lane_pair_sum(float v)
 // A workgroup drains its own XCD's queue first and then steals from the
 // others.  Slot k of queue x is slot k % chunk of chunk x + kQueues *
 // (k / chunk); slots past the last item of a (batch, head) are skipped, and
-// `order` permutes the items inside each chunk.
+// `order` permutes the items inside each chunk.  A workgroup whose queue
+// runs dry reads all counters at once to find the queues that still hold
+// slots, so the end of a launch costs two round trips per workgroup, not
+// one atomic per queue.
 struct WorkQueue {
     uint32_t *ctr;
     const __attribute__((address_space(4))) int32_t *order;
@@ -51,24 +54,59 @@ struct WorkQueue {
     {
     }
 
+    // Slots of queue q.
+    __device__ long long queue_len(int q) const
+    {
+        const int chunks_q = total_chunks > q ? (total_chunks - q + kQueues - 1) / kQueues : 0;
+        return (long long)chunks_q * chunk;
+    }
+
     // Next item of the workgroup (wave-uniform results); false when every
     // queue is drained.  `x` is the queue being drained (start: this XCD),
-    // `tries` how many queues have been left behind.
+    // `tries` how many queues have been found drained.
     __device__ bool next(int &x, int &tries, int *slot, int &bh, int &item)
     {
         for (;;) {
             if (tries >= kQueues)
                 return false;
-            const int chunks_x = total_chunks > x ? (total_chunks - x + kQueues - 1) / kQueues : 0;
-            const long long len = (long long)chunks_x * chunk;
+            const long long len = queue_len(x);
             if (threadIdx.x == 0)
                 *slot = (int)atomicAdd(&ctr[x], 1u);
             __syncthreads();
             const int k = __builtin_amdgcn_readfirstlane(*slot);
             __syncthreads();
             if (k >= len) {
-                x = (x + 1) % kQueues;
+                // Queue x is drained.  Read every queue's counter at once
+                // (coherent loads, one round trip) and move to the next
+                // queue after x that still has slots, instead of trying the
+                // others one atomic at a time; none left ends the walk.  A
+                // counter only grows, so a queue seen drained stays drained,
+                // and one seen with slots is checked again by its atomic.
                 ++tries;
+                if (threadIdx.x < 64) {
+                    const int q = threadIdx.x;
+                    bool has = false;
+                    if (q < kQueues)
+                        has = (long long)__hip_atomic_load(&ctr[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                              queue_len(q);
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(has);
+                    if (threadIdx.x == 0)
+                        *slot = (int)m;
+                }
+                __syncthreads();
+                const int m = __builtin_amdgcn_readfirstlane(*slot);
+                __syncthreads();
+                if (m == 0)
+                    return false;
+                int y = x;
+                for (int i = 1; i < kQueues; ++i) {
+                    const int c = (x + i) % kQueues;
+                    if ((m >> c) & 1) {
+                        y = c;
+                        break;
+                    }
+                }
+                x = y;
                 continue;
             }
             const int g = x + kQueues * (k / chunk);
