@@ -260,15 +260,19 @@ void attn_fwd_bf16(AttnArgs a)
 
             // ---- element mask of a partly kept tile ----
             if (em >= 0) {
+                // element i of 32-key step kb4 is key 8 (i / 4) + 4 hh + i % 4:
+                // its bit, sign-extended, selects the score or -inf
                 const uint32_t words[4] = {mw.x, mw.y, mw.z, mw.w};
 #pragma unroll
-                for (int kb4 = 0; kb4 < 4; ++kb4)
+                for (int kb4 = 0; kb4 < 4; ++kb4) {
+                    const int w = (int)(words[kb4] >> (4 * hh));
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const int bit = 8 * (i >> 2) + 4 * hh + (i & 3);
-                        if (!((words[kb4] >> bit) & 1u))
-                            s[kb4][i] = kNegInf;
+                        const int keep = __builtin_amdgcn_sbfe(w, 8 * (i >> 2) + (i & 3), 1);
+                        s[kb4][i] = __int_as_float((__float_as_int(s[kb4][i]) & keep) |
+                                                   (__float_as_int(kNegInf) & ~keep));
                     }
+                }
             }
             // ---- streaming softmax (base 2) ----
             // At D = 64, once every row of the wave has a finite maximum, a
