@@ -35,10 +35,10 @@
 //   - operand fragments are read one step ahead of the MFMAs that use them;
 //   - the accumulator is rescaled only when some row's maximum grows by more
 //     than 2^8 (wave-uniform test); otherwise the stale maximum is kept, which
-//     leaves probabilities <= 2^8 and the result exact up to rounding.  At
-//     D = 64 the tile maximum is not even looked for once every row has one:
-//     the exponentials are taken against the maximum in use and redone after
-//     a rescale only when a lane's sum of them passes 2^32;
+//     leaves probabilities <= 2^8 and the result exact up to rounding.  The
+//     tile maximum is not even looked for once every row has one: the
+//     exponentials are taken against the maximum in use and redone after a
+//     rescale only when a lane's sum of them passes 2^32;
 //   - partly kept tiles get their element bitmask applied to the scores; the
 //     waves of a query block that does not keep a tile of the union skip it;
 //   - workgroups are persistent and pop items from per-XCD queues of chunks
@@ -275,16 +275,17 @@ void attn_fwd_bf16(AttnArgs a)
                 }
             }
             // ---- streaming softmax (base 2) ----
-            // At D = 64, once every row of the wave has a finite maximum, a
-            // tile's probabilities are first taken against the maximum in
-            // use without looking for the tile's own maximum; only if some
-            // lane's sum of them passes 2^32 (a score more than 26 above the
+            // Once every row of the wave has a finite maximum, a tile's
+            // probabilities are first taken against the maximum in use
+            // without looking for the tile's own maximum; only if some lane's
+            // sum of them passes 2^32 (a score more than 26 above the
             // maximum, in log2 units) is the maximum taken and the tile's
             // exponentials redone.  Probabilities up to 2^32 leave bf16 and
             // the fp32 sums far from overflow, and the result is the same
-            // up to rounding.  (At D = 128 the second exponential loop does
-            // not fit the registers.)
-            const bool lazy = D == 64 && !__builtin_amdgcn_ballot_w64(m == kNegInf);
+            // up to rounding.  At D = 64 the scores stay in registers for the
+            // redo; at D = 128 they do not fit beside the probabilities, and
+            // the redo recomputes them from the tile, which is still in LDS.
+            const bool lazy = !__builtin_amdgcn_ballot_w64(m == kNegInf);
             auto take_max = [&]() {
                 float mx = kNegInf;
 #pragma unroll
@@ -333,6 +334,32 @@ void attn_fwd_bf16(AttnArgs a)
                 take_max();
             exps();
             if (lazy && __builtin_amdgcn_ballot_w64(!(ls[0] + ls[1] <= 0x1p32f))) {
+                if constexpr (D == 128) {
+                    // scores and element mask again, as above (this path is
+                    // rare, so its operand reads are not pipelined)
+#pragma unroll
+                    for (int ks = 0; ks < G::NKS; ++ks)
+#pragma unroll
+                        for (int kb4 = 0; kb4 < 4; ++kb4) {
+                            const bf16x8 kk = *(const bf16x8 LDS_AS *)(tK + koff[ks] + kb4 * 32 * G::ROWB);
+                            s[kb4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qf[ks], ks == 0 ? s0 : s[kb4],
+                                                                             0, 0, 0);
+                        }
+                    if (em >= 0) {
+                        const uint4 mr = ((const uint4 *)a.mask.emask)[(size_t)em * kBlock + w4 * 32 + lq];
+                        const uint32_t words[4] = {mr.x, mr.y, mr.z, mr.w};
+#pragma unroll
+                        for (int kb4 = 0; kb4 < 4; ++kb4) {
+                            const int w = (int)(words[kb4] >> (4 * hh));
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) {
+                                const int keep = __builtin_amdgcn_sbfe(w, 8 * (i >> 2) + (i & 3), 1);
+                                s[kb4][i] = __int_as_float((__float_as_int(s[kb4][i]) & keep) |
+                                                           (__float_as_int(kNegInf) & ~keep));
+                            }
+                        }
+                    }
+                }
                 take_max();
                 exps();
             }
