@@ -529,7 +529,6 @@ void k_bwd_dq(BwdArgs a)
                 continue;
             const char LDS_AS *tK = (const char LDS_AS *)(buf == 0 ? sK0 : sK1);
             const char LDS_AS *tV = (const char LDS_AS *)(buf == 0 ? sV0 : sV1);
-            const uint32_t words[4] = {mw.x, mw.y, mw.z, mw.w};
 
 #pragma unroll 1
             for (int hf = 0; hf < 2; ++hf) {
@@ -552,12 +551,17 @@ void k_bwd_dq(BwdArgs a)
                     }
                 // element i of s[kb] is key 32 (2 hf + kb) + 8 (i / 4) + 4 hh + i % 4
                 if (em >= 0) {
+                    // words selected in registers: indexed by the loop
+                    // counter, a 4-word array was placed in LDS, and its
+                    // store, issued after the next tile's copies, waited
+                    // for them
+                    const uint32_t words[2] = {hf ? mw.z : mw.x, hf ? mw.w : mw.y};
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                         for (int i = 0; i < 16; ++i) {
                             const int bit = 8 * (i >> 2) + 4 * hh + (i & 3);
-                            if (!((words[2 * hf + kb] >> bit) & 1u))
+                            if (!((words[kb] >> bit) & 1u))
                                 s[kb][i] = kNegInf;
                         }
                 }
