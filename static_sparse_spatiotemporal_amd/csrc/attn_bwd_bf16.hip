@@ -20,12 +20,14 @@
 //                accumulates dQ.
 // Both main kernels recompute S and dP with v_mfma_f32_32x32x16_bf16 and
 // keep the operand that stays fixed for the workgroup (K and V, or Q and dO)
-// in registers; the
-// streamed tiles are copied HBM -> LDS with
+// in registers; the streamed tiles are copied HBM -> LDS with
 // global_load_lds_dwordx4 into double buffers (one LDS array each, named
 // statically in every step), XOR-swizzled so that both the row reads
 // (ds_read_b128) and the transposed reads (ds_read_b64_tr_b16) of one tile
-// are free of bank conflicts (see swz).
+// are free of bank conflicts (see swz).  A partly kept block's element mask
+// words are loaded before the tile's wait (dQ: one 16-byte row per lane;
+// dK/dV at D = 64: two words per lane, staged in the wave's own LDS words),
+// never behind the next tile's copies.
 #include "attn_common.h"
 
 namespace tra {
