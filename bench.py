@@ -39,6 +39,9 @@ def kernel_source_digest() -> str:
     for fn in ("attn_fwd_bf16.hip", "attn_common.h", "tra_internal.h", "tra_sched.h", "tra_sched.cpp"):
         with open(os.path.join(ROOT, "static_sparse_spatiotemporal_amd", "csrc", fn), "rb") as f:
             h.update(f.read())
+    # the forward's compiler options decide its code as much as its source
+    from static_sparse_spatiotemporal_amd import _build
+    h.update(" ".join(_build.FILE_FLAGS.get("attn_fwd_bf16.hip", [])).encode())
     return h.hexdigest()[:16]
 
 
