@@ -173,8 +173,12 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
  * masked (impossible for the families above) get O = 0 and LSE = -inf.
  *
  * The mask is shared by every (b, h).  Asynchronous on hip_stream; allocates
- * nothing.  The mask holds the work-queue counter of the kernel, so calls
- * that use the same mask must not run concurrently (same stream is fine).
+ * nothing.  The mask holds the work-queue counters of the kernel and, for
+ * launches with few work items per compute unit, the records through which
+ * the two halves of an item split over its key blocks are combined (in a
+ * fixed order: results are the same bit for bit on every call).  Calls that
+ * use the same mask must therefore not run concurrently (same stream is
+ * fine).
  * B == 0 or H == 0 returns TRA_OK without launching.
  * Errors: TRA_ERR_INVALID (null tensor/mask/data), TRA_ERR_SHAPE (shapes
  * disagree or N != n), TRA_ERR_UNSUPPORTED (D not 64/128, mixed dtypes,

@@ -272,7 +272,8 @@ void k_bwd_dkdv(BwdArgs a)
 
     WorkQueue wq(f.mask.queue, f.mask.t_pair_order, f.mask.t_npairs, kPairChunk, f.B * f.H);
     int wx = xcd_id(), wtries = 0, bh = 0, pair = 0;
-    while (wq.next(wx, wtries, &sItem, bh, pair)) {
+    int whalf = -1, wsplit = 0;
+    while (wq.next(wx, wtries, &sItem, bh, pair, whalf, wsplit)) {
         const int kcol = pair_cols[2 * pair + half];  // -1: this half idles
         const bool active = kcol >= 0;
         const int u0 = pair_ptr[pair], u1 = pair_ptr[pair + 1];
@@ -530,7 +531,8 @@ void k_bwd_dq(BwdArgs a)
 
     WorkQueue wq(f.mask.queue, f.mask.pair_order, f.mask.npairs, kPairChunk, f.B * f.H);
     int wx = xcd_id(), wtries = 0, bh = 0, pair = 0;
-    while (wq.next(wx, wtries, &sItem, bh, pair)) {
+    int whalf = -1, wsplit = 0;
+    while (wq.next(wx, wtries, &sItem, bh, pair, whalf, wsplit)) {
         const int row = pair_rows[2 * pair + half];
         const bool active = row >= 0;
         const int u0 = pair_ptr[pair], u1 = pair_ptr[pair + 1];

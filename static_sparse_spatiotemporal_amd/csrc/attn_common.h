@@ -43,28 +43,44 @@ __device__ inline float lane_pair_sum(float v)
 // runs dry reads all counters at once to find the queues that still hold
 // slots, so the end of a launch costs two round trips per workgroup, not
 // one atomic per queue.
+//
+// With `tail` set, the last chunk of every queue is handed out in halves:
+// its slots come twice, as (item, half 0) and (item, half 1), each half
+// taking one half of the item's key blocks.  A launch with few items per
+// workgroup otherwise ends with a round of whole items on some compute
+// units while the others idle; halves shorten that round.  The split
+// index of such a slot (queue * chunk + position in the chunk, below
+// kQueues * chunk) names where the two halves meet (see the forward).
 struct WorkQueue {
     uint32_t *ctr;
     const __attribute__((address_space(4))) int32_t *order;
     int per_bh, chunk, nch, total_chunks;
+    bool tail;
 
-    __device__ WorkQueue(uint32_t *queue, const int32_t *order_, int per_bh_, int chunk_, int bh_count)
+    __device__ WorkQueue(uint32_t *queue, const int32_t *order_, int per_bh_, int chunk_, int bh_count,
+                         bool tail_ = false)
         : ctr(queue), order((const __attribute__((address_space(4))) int32_t *)order_), per_bh(per_bh_),
-          chunk(chunk_), nch((per_bh_ + chunk_ - 1) / chunk_), total_chunks(bh_count * nch)
+          chunk(chunk_), nch((per_bh_ + chunk_ - 1) / chunk_), total_chunks(bh_count * nch), tail(tail_)
     {
     }
 
-    // Slots of queue q.
+    __device__ int queue_chunks(int q) const
+    {
+        return total_chunks > q ? (total_chunks - q + kQueues - 1) / kQueues : 0;
+    }
+
+    // Slots of queue q (its last chunk twice over in tail mode).
     __device__ long long queue_len(int q) const
     {
-        const int chunks_q = total_chunks > q ? (total_chunks - q + kQueues - 1) / kQueues : 0;
-        return (long long)chunks_q * chunk;
+        const int chunks_q = queue_chunks(q);
+        return (long long)(chunks_q + (tail && chunks_q > 0 ? 1 : 0)) * chunk;
     }
 
     // Next item of the workgroup (wave-uniform results); false when every
     // queue is drained.  `x` is the queue being drained (start: this XCD),
-    // `tries` how many queues have been found drained.
-    __device__ bool next(int &x, int &tries, int *slot, int &bh, int &item)
+    // `tries` how many queues have been found drained.  `half` is -1 for a
+    // whole item, else 0 or 1 with `split` the item's split index.
+    __device__ bool next(int &x, int &tries, int *slot, int &bh, int &item, int &half, int &split)
     {
         for (;;) {
             if (tries >= kQueues)
@@ -109,8 +125,18 @@ struct WorkQueue {
                 x = y;
                 continue;
             }
-            const int g = x + kQueues * (k / chunk);
-            const int pos = (g % nch) * chunk + k % chunk;
+            int g = x + kQueues * (k / chunk), j = k % chunk;
+            half = -1;
+            if (tail) {
+                const int last = queue_chunks(x) - 1;
+                if (k >= last * chunk) {
+                    j = (k - last * chunk) >> 1;
+                    half = (k - last * chunk) & 1;
+                    g = x + kQueues * last;
+                    split = x * chunk + j;
+                }
+            }
+            const int pos = (g % nch) * chunk + j;
             if (pos >= per_bh)
                 continue;
             bh = g / nch;

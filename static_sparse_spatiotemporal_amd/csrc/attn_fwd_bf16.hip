@@ -53,6 +53,10 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
+// Items per resident workgroup below which the tail mode is used.
+constexpr long long kTailItemsPerGroup = 16;
+static_assert(kSplitLaneFloats >= 128 / 32 * 16 + 2 && kSplitRecFloats == kWaves * 64 * kSplitLaneFloats,
+              "split record layout");
 
 template <int D>
 struct Geo {
@@ -81,6 +85,10 @@ __device__ inline int v_swz(int row)
 
 __device__ inline void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Relaxed agent-scope accesses of the split records (see the tail mode).
+__device__ inline void store_agent(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline float load_agent(float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
 // Copy one 128-row tile of X (rows key0 ..) into LDS.  Copy instruction i of
 // wave w fills bytes (8 i + w) KB .. of the tile: rows crow0 + 8 RPI i, where
 // crow0 = w RPI + lane / CPR.  `lane_off` is this lane's element offset
@@ -108,7 +116,7 @@ __device__ inline void copy_tile(const __bf16 *X, int64_t stride, int key0, int 
     }
 }
 
-template <int D, bool STREAM>
+template <int D, bool STREAM, bool TAIL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(AttnArgs a)
 {
@@ -170,8 +178,9 @@ void attn_fwd_bf16(AttnArgs a)
     cint *u_em = (cint *)a.mask.u_em;
 
     // One work item: query block `row` of this half (-1: idle) over the key
-    // blocks of schedule entries u0 .. u1 - 1.
-    auto item = [&](int bh, int row, int u0, int u1, int split) {
+    // blocks of schedule entries u0 .. u1 - 1.  tslot >= 0: half tslot & 1
+    // of a split item (tail mode), merged through split record tslot >> 1.
+    auto item = [&](int bh, int row, int u0, int u1, int split, int tslot) {
         const bool active = row >= 0;
         const int b = bh / a.H, h = bh - b * a.H;
         const __bf16 *Qp = (const __bf16 *)a.q + b * a.sq[0] + h * a.sq[1];
@@ -392,6 +401,82 @@ void attn_fwd_bf16(AttnArgs a)
             __builtin_amdgcn_sched_barrier(0);
         }
 
+        // ---- tail mode: the two halves of a split item meet ----
+        // Each half leaves m, its lane sums and its unnormalised O^T
+        // fragments (each lane its own registers, so the other half reads
+        // them back in the same order); the first to finish then leaves, and
+        // the second takes the other's state in, both rescaled to the larger
+        // maximum, and writes the output.  The sum is taken in half order,
+        // not finishing order, so the output does not depend on which half
+        // ends first.  The halves may run on different XCDs, whose L2s are
+        // not coherent for ordinary accesses: the records are written and
+        // read with agent-scope atomic accesses, which reach the coherence
+        // point one by one.  An agent-scope fence would instead write back
+        // and invalidate the whole L2, throwing away the K/V tiles the
+        // XCD's other workgroups are streaming.
+        if (TAIL && tslot >= 0) {
+            constexpr int F = G::NDB * 16;
+            const int rslot = tslot >> 1;
+            const bool first_half = (tslot & 1) == 0;
+            // each half leaves its state in its own record (record tslot);
+            // the second reads the other's (tslot ^ 1)
+            float *rec = a.mask.split_ws + (int64_t)tslot * kSplitRecFloats + (int64_t)wave * 64 * kSplitLaneFloats;
+            if (active) {
+#pragma unroll
+                for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                        f32x4 v;
+#pragma unroll
+                        for (int x = 0; x < 4; ++x)
+                            v[x] = o[db][4 * i4 + x];
+#pragma unroll
+                        for (int x = 0; x < 4; ++x)
+                            store_agent(rec + ((db * 4 + i4) * 4 + x) * 64 + lane, v[x]);
+                    }
+                store_agent(rec + F * 64 + lane, m);
+                store_agent(rec + (F + 1) * 64 + lane, l);
+            }
+            // every wave's record stores (and its last tile copy) complete
+            // before the counter moves
+            wait_copies();
+            __syncthreads();
+            if (tid == 0)
+                sItem = (int)__hip_atomic_fetch_add(&a.mask.split_ctr[rslot], 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            const int other_done = __builtin_amdgcn_readfirstlane(sItem);
+            __syncthreads();
+            if (other_done == 0)
+                return;
+            if (tid == 0)
+                __hip_atomic_store(&a.mask.split_ctr[rslot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            rec = a.mask.split_ws + (int64_t)(tslot ^ 1) * kSplitRecFloats + (int64_t)wave * 64 * kSplitLaneFloats;
+            if (active) {
+                const float mo = load_agent(rec + F * 64 + lane), lo = load_agent(rec + (F + 1) * 64 + lane);
+                const float m0 = first_half ? m : mo, m1 = first_half ? mo : m;
+                const float l0 = first_half ? l : lo, l1 = first_half ? lo : l;
+                const float mn = fmaxf(m0, m1);
+                const float mb = mn == kNegInf ? 0.f : mn;
+                const float a0 = m0 == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m0 - mb) * c2);
+                const float a1 = m1 == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m1 - mb) * c2);
+#pragma unroll
+                for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4) {
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            const float v = load_agent(rec + ((db * 4 + i4) * 4 + x) * 64 + lane);
+                            const float o0 = first_half ? o[db][4 * i4 + x] : v;
+                            const float o1 = first_half ? v : o[db][4 * i4 + x];
+                            o[db][4 * i4 + x] = __builtin_fmaf(o1, a1, o0 * a0);
+                        }
+                    }
+                l = __builtin_fmaf(l1, a1, l0 * a0);
+                m = mn;
+            }
+        }
+
         // ---- epilogue: O = acc / l, LSE = ln 2 * (m c2 + log2 l) ----
         if (STREAM && active) {
             // normalised partial output and log2-sum-exp of this key split
@@ -443,13 +528,29 @@ void attn_fwd_bf16(AttnArgs a)
         const int row = 2 * pair + half < a.mask.nqb ? 2 * pair + half : -1;
         const int u0 = split * a.split_tiles;
         const int u1 = u0 + a.split_tiles < a.nkv_tiles ? u0 + a.split_tiles : a.nkv_tiles;
-        item(bh, row, u0, u1, split);
+        item(bh, row, u0, u1, split, -1);
         wait_copies();  // the last step's copy must land before the workgroup ends
     } else {
-        WorkQueue wq(a.mask.queue, a.mask.pair_order, a.mask.npairs, kPairChunk, a.B * a.H);
-        int wx = xcd_id(), wtries = 0, bh = 0, pair = 0;
-        while (wq.next(wx, wtries, &sItem, bh, pair))
-            item(bh, pair_rows[2 * pair + half], pair_ptr[pair], pair_ptr[pair + 1], 0);
+        WorkQueue wq(a.mask.queue, a.mask.pair_order, a.mask.npairs, kPairChunk, a.B * a.H, TAIL);
+        int wx = xcd_id(), wtries = 0, bh = 0, pair = 0, whalf = -1, wsplit = 0;
+        while (wq.next(wx, wtries, &sItem, bh, pair, whalf, wsplit)) {
+            int u0 = pair_ptr[pair], u1 = pair_ptr[pair + 1], tslot = -1;
+            if (TAIL && whalf >= 0) {
+                // a half of the queue's last chunk: an item too short to
+                // split runs whole as half 0
+                if (u1 - u0 >= a.split_min) {
+                    const int mid = u0 + (u1 - u0) / 2;
+                    if (whalf == 0)
+                        u1 = mid;
+                    else
+                        u0 = mid;
+                    tslot = 2 * wsplit + whalf;
+                } else if (whalf == 1) {
+                    continue;
+                }
+            }
+            item(bh, pair_rows[2 * pair + half], u0, u1, 0, tslot);
+        }
         // The last step of an item re-copies its tile into the free buffer.
         // A wave's copies land in issue order, so the next item's first copy
         // still wins; only the workgroup's end has to wait for the last one.
@@ -534,20 +635,35 @@ __global__ __launch_bounds__(256) void k_ring_copy(RingCopy k, RingCopy v, int64
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t st)
+hipError_t launch_attn_bf16(const AttnArgs &a_in, hipStream_t st)
 {
+    AttnArgs a = a_in;
     const long long items = (long long)a.B * a.H * a.mask.npairs;
-    return a.D == 128 ? launch_persistent(attn_fwd_bf16<128, false>, kThreads, items, a, st)
-                      : launch_persistent(attn_fwd_bf16<64, false>, kThreads, items, a, st);
+    const void *kern =
+        a.D == 128 ? (const void *)attn_fwd_bf16<128, false, false> : (const void *)attn_fwd_bf16<64, false, false>;
+    long long grid = 0;
+    const hipError_t e = resident_workgroups(kern, kThreads, &grid);
+    if (e != hipSuccess)
+        return e;
+    // Few items per workgroup, some long enough to split: the launch would
+    // end with a round of whole items on some compute units while the rest
+    // idle, so the queues' last chunks run as halves.  With many items that
+    // round is short anyway.
+    a.tail_split = items < kTailItemsPerGroup * grid && a.max_pair_tiles >= a.split_min ? 1 : 0;
+    if (a.tail_split)
+        return a.D == 128 ? launch_persistent(attn_fwd_bf16<128, false, true>, kThreads, items, a, st)
+                          : launch_persistent(attn_fwd_bf16<64, false, true>, kThreads, items, a, st);
+    return a.D == 128 ? launch_persistent(attn_fwd_bf16<128, false, false>, kThreads, items, a, st)
+                      : launch_persistent(attn_fwd_bf16<64, false, false>, kThreads, items, a, st);
 }
 
 hipError_t launch_attn_stream_bf16(const AttnArgs &a, hipStream_t st)
 {
     const long long items = (long long)a.B * a.H * a.stream_pairs * a.nsplit;
     if (a.D == 128)
-        hipLaunchKernelGGL((attn_fwd_bf16<128, true>), dim3((unsigned)items), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((attn_fwd_bf16<128, true, false>), dim3((unsigned)items), dim3(kThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((attn_fwd_bf16<64, true>), dim3((unsigned)items), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((attn_fwd_bf16<64, true, false>), dim3((unsigned)items), dim3(kThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

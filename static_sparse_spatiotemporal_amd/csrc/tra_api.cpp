@@ -82,6 +82,8 @@ void free_mask_buffers(tra_mask *m)
     dev_free(m->u_em);
     dev_free(m->pair_order);
     dev_free(m->queue);
+    dev_free(m->split_ctr);
+    dev_free(m->split_ws);
     dev_free(m->t_pair_cols);
     dev_free(m->t_pair_ptr);
     dev_free(m->t_u_row);
@@ -124,6 +126,8 @@ void fill_attn_args(tra::AttnArgs &a, const tra_tensor *Q, const tra_tensor *K, 
     a.mask.u_em = mask->u_em;
     a.mask.pair_order = mask->pair_order;
     a.mask.queue = mask->queue;
+    a.mask.split_ctr = mask->split_ctr;
+    a.mask.split_ws = mask->split_ws;
     a.mask.nqb = (int32_t)mask->info.nqb;
     a.mask.npairs = mask->npairs;
     a.mask.t_pair_cols = mask->t_pair_cols;
@@ -136,6 +140,9 @@ void fill_attn_args(tra::AttnArgs &a, const tra_tensor *Q, const tra_tensor *K, 
     a.part_o = nullptr;
     a.part_lse = nullptr;
     a.nsplit = a.split_tiles = a.nkv_tiles = a.stream_pairs = 0;
+    a.tail_split = 0;
+    a.split_min = 8;
+    a.max_pair_tiles = mask->max_pair_tiles;
 }
 
 }  // namespace
@@ -343,12 +350,15 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
     TRA_HIP(dev_alloc(&m->order, nqb));
     TRA_HIP(dev_alloc(&m->bitmap, (size_t)nqb * words));
     TRA_HIP(dev_alloc(&m->queue, tra::kQueueWords));
+    TRA_HIP(dev_alloc(&m->split_ctr, tra::kSplitSlots));
+    TRA_HIP(dev_alloc(&m->split_ws, (size_t)2 * tra::kSplitSlots * tra::kSplitRecFloats));
     TRA_HIP(dev_alloc(&part_ptr_d, nqb + 1));
     TRA_HIP(dev_alloc(&part_list, (size_t)npart));
     TRA_HIP(hipMemcpyAsync(m->row_ptr, h_row_ptr.data(), (nqb + 1) * sizeof(int32_t), hipMemcpyHostToDevice, st));
     TRA_HIP(hipMemcpyAsync(part_ptr_d, h_part_ptr.data(), (nqb + 1) * sizeof(int32_t), hipMemcpyHostToDevice, st));
     TRA_HIP(hipMemcpyAsync(m->order, h_order.data(), nqb * sizeof(int32_t), hipMemcpyHostToDevice, st));
     TRA_HIP(hipMemsetAsync(m->queue, 0, tra::kQueueWords * sizeof(uint32_t), st));
+    TRA_HIP(hipMemsetAsync(m->split_ctr, 0, tra::kSplitSlots * sizeof(uint32_t), st));
     TRA_HIP(tra::launch_compact(nqb, nkb, cls, m->row_ptr, part_ptr_d, m->col_idx, m->emask_idx, part_list, st));
     TRA_HIP(tra::launch_fill_emask(d, (int)npart, part_list, nkb, m->emask, st));
     TRA_HIP(tra::launch_bitmap(nqb, nkb, words, cls, m->bitmap, st));
@@ -363,6 +373,8 @@ tra_status tra_build_mask(int64_t f, int64_t s, int32_t kind, const tra_mask_par
     }
     ps = tra::build_pairs(nqb, s, h_row_ptr, h_col, h_em);
     m->npairs = (int32_t)(ps.rows.size() / 2);
+    for (int32_t p = 0; p < m->npairs; ++p)
+        m->max_pair_tiles = std::max(m->max_pair_tiles, ps.ptr[p + 1] - ps.ptr[p]);
     TRA_HIP(dev_alloc(&m->pair_rows, ps.rows.size()));
     TRA_HIP(dev_alloc(&m->pair_ptr, ps.ptr.size()));
     TRA_HIP(dev_alloc(&m->u_col, ps.col.size()));

@@ -14,6 +14,14 @@ namespace tra {
 // finished-workgroup counter.
 constexpr int kQueues = 8;
 constexpr int kQueueWords = 16;
+// Split items of the forward's tail mode (see WorkQueue): at most one per
+// slot of a queue's last chunk.  Each half leaves its partial state
+// (unnormalised O^T fragments, row maximum and lane sums, in each lane's
+// register order) in a record of its own, 2 x split + half, which the half
+// that finishes second reads.
+constexpr int kSplitSlots = kQueues * kPairChunk;
+constexpr int kSplitLaneFloats = 128 / 32 * 16 + 2;          // O^T fragments at D = 128, m, l
+constexpr int64_t kSplitRecFloats = 8 * 64 * kSplitLaneFloats;  // 8 waves x 64 lanes
 
 // Mask family as seen by device code.
 struct MaskDesc {
@@ -46,6 +54,8 @@ struct MaskDev {
     const int32_t *u_em;       // [nunion][2] emask index per member
     const int32_t *pair_order; // [npairs] chunk-wise heaviest-first pairs
     uint32_t *queue;           // [kQueueWords] XCD queue counters, finished-group counter
+    uint32_t *split_ctr;       // [kSplitSlots] halves of a split item done (reset by the second)
+    float *split_ws;           // [2 * kSplitSlots][kSplitRecFloats] partial state of each half
     int32_t nqb;
     int32_t npairs;
     // The same schedule over key blocks (columns of the block mask), for the
@@ -79,7 +89,10 @@ struct tra_mask {
     int32_t *u_em;
     int32_t *pair_order;
     int32_t npairs;
+    int32_t max_pair_tiles;  // longest item of the pair schedule (key blocks)
     uint32_t *queue;
+    uint32_t *split_ctr;
+    float *split_ws;
     int32_t *t_pair_cols;
     int32_t *t_pair_ptr;
     int32_t *t_u_row;
@@ -130,6 +143,10 @@ struct AttnArgs {
     float *part_o;     // [nsplit][B * H * N][D]
     float *part_lse;   // [nsplit][B * H * N]
     int32_t nsplit, split_tiles, nkv_tiles, stream_pairs;
+    // Tail mode of the masked call (see WorkQueue): items of the queues'
+    // last chunks with at least split_min key blocks run as two halves.
+    int32_t tail_split, split_min;
+    int32_t max_pair_tiles;  // longest item of the pair schedule (key blocks)
 };
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t st);
 // Split-key launch (see AttnArgs) followed by the merge into a.o / a.lse.

@@ -1,6 +1,6 @@
 """Error paths of the allocating entry points, driven by failure injection.
 
-tra_build_mask makes about 25 device allocations and tra_kvcache_create 4;
+tra_build_mask makes about 27 device allocations and tra_kvcache_create 4;
 a failure at any of them must return TRA_ERR_OOM, release everything the
 call had allocated so far, and leave the library able to build the same
 object afterwards.  The injection (include/tra_debug.h) makes the k-th

@@ -368,3 +368,39 @@ def test_mask_serves_other_batch_and_head_counts(tra):
     torch.cuda.synchronize()
     assert torch.equal(again, out1)
     mask.free()
+
+
+TAIL = [
+    # (kind, f, s, granularity, extra, B, H, D, dtype, ramp): few items per
+    # workgroup, so the queues' last chunks run as two halves of their key
+    # blocks that meet in the second half to finish
+    ("swa", 24, 256, "element", dict(window=10), 1, 3, 64, "bf16", False),
+    ("radial", 16, 256, "element", {}, 1, 2, 128, "bf16", False),
+    ("radial", 16, 256, "element", dict(sink_frames=1), 1, 2, 64, "bf16", False),
+    ("swa", 12, 256, "element", dict(window=12), 1, 2, 128, "bf16", True),
+    ("swa", 12, 256, "element", dict(window=12), 1, 2, 64, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("case", TAIL, ids=lambda c: f"{c[0]}-f{c[1]}-s{c[2]}-D{c[7]}-{'ramp' if c[9] else 'gauss'}")
+def test_tail_split_halves(tra, case):
+    """Items split over their key blocks: the halves' partial states are
+    combined in half order, so the output matches the oracle and is the same
+    bit for bit on every call, whichever half ends first.  The ramped inputs
+    put the two halves' row maxima hundreds of log2 units apart (one half's
+    weights vanish against the other's); the radial mask leaves rows that
+    keep no key of one half."""
+    kind, f, s, gran, extra, B, H, D, dt, ramp = case
+    w = workloads.Workload(f"tail_{kind}_f{f}_s{s}", kind, gran, f, s, B, H, D, dt, seed=900 + f + D, **extra)
+    if ramp:
+        q, k, v = workloads.make_ramp_qkv(w, span=240.0, device="cuda")
+    else:
+        q, k, v = workloads.make_qkv(w, device="cuda")
+    mask = build(tra, w)
+    eo, el, out, lse = run_and_compare(tra, w, q, k, v, mask=mask)
+    assert eo <= TOL_O[dt] and el <= 1
+    for _ in range(3):
+        o2, l2 = tra.sparse_attn_fwd(q, k, v, mask)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, out) and torch.equal(l2, lse)
+    mask.free()
